@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of exact tiled attention on one MI355X.
+
+One step = forward + backward of bf16 attention at hidden size 2048
+(H = 16 heads of D = 128), B * S = 16384 tokens, for every
+S in {512, 1K, 2K, 4K, 8K, 16K}, non-causal and causal: 12 fwd+bwd passes.
+The headline value is their total algorithmic work over their total time,
+in TFLOP/s, with the work counted as 4 D per visible (query, key) pair for
+the forward and 10 D for the backward.
+
+Printed as one JSON line, with
+  roofline     — the kernel that takes the most time in the timed region,
+                 its algorithmic TFLOP/s (measured with HIP events around
+                 each launch on the launch stream) against the dense bf16
+                 MFMA peak;
+  cpu_baseline — the float64 numpy oracle timed on this host on a bounded
+                 sample of the same workload (one (batch, head) slice per
+                 sequence length up to 4K);
+  decode       — the paged KV-cache decode step (B = 8, Hq = 32, Hkv = 8,
+                 D = 128, cache lengths ~ U[1K, 64K], page 256, rotary,
+                 16 splits) in HBM GB/s.
+
+Modes: ``--copy-calibration`` runs a plain device copy of known size (for
+scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters); ``--decode-only`` and
+``--fwdbwd-only`` restrict the run for profiling.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+SEQLENS = (512, 1024, 2048, 4096, 8192, 16384)
+H, D, TOKENS = 16, 128, 16384
+METRIC = "attention TFLOPs/s fwd+bwd (bf16, hd128, S=512–16K); decode KV GB/s"
+
+
+def pairs_causal(S):
+    return S * (S + 1) // 2
+
+
+def visible_pairs(B, H_, S, causal):
+    return B * H_ * (pairs_causal(S) if causal else S * S)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+def run_fwdbwd(args, torch, fa):
+    from workloads import cfg2
+    dev = torch.device("cuda:0")
+    cases = []
+    for S in SEQLENS:
+        c = cfg2(S, H, D, False)
+        B = TOKENS // S
+        t = dict(S=S, B=B, q=c.q.to(dev), k=c.k.to(dev), v=c.v.to(dev), do=c.dout.to(dev))
+        t["out"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty(B, H, S, device=dev, dtype=torch.float32)
+        t["dq"] = torch.empty_like(t["q"])
+        t["dk"] = torch.empty_like(t["k"])
+        t["dv"] = torch.empty_like(t["v"])
+        ws = fa.lib().fa_bwd_workspace_size(B, S, S, H, H, D, 0)
+        t["ws"] = torch.empty(ws, device=dev, dtype=torch.uint8)
+        cases.append(t)
+        log(f"inputs ready S={S}")
+    scale = 1.0 / math.sqrt(D)
+
+    def one(t, causal):
+        fa.fa_fwd(t["q"], t["k"], t["v"], out=t["out"], lse=t["lse"], scale=scale, causal=causal)
+        fa.fa_bwd(t["q"], t["k"], t["v"], t["out"], t["do"], t["lse"], dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                  scale=scale, causal=causal, workspace=t["ws"])
+
+    def step():
+        for t in cases:
+            for causal in (False, True):
+                one(t, causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-config timing (separate, untimed for the headline)
+    per = []
+    for t in cases:
+        for causal in (False, True):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            e0.record()
+            for _ in range(reps):
+                one(t, causal)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
+            per.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
+                        "tflops": round(fl / ms / 1e9, 1)})
+    # timed region
+    fa.profiler_enable(4096)
+    fa.profiler_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = fa.profiler_read()
+    fa.profiler_disable()
+    flops_step = sum(14 * D * visible_pairs(t["B"], H, t["S"], c) for t in cases for c in (False, True))
+    pairs_step = sum(visible_pairs(t["B"], H, t["S"], c) for t in cases for c in (False, True))
+    value = flops_step * args.steps / wall / 1e12
+    # algorithmic flops per kernel kind: fwd 4D, dK/dV 8D (S, dP, dV, dK), dQ 2D per pair
+    per_pair = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 2 * D, "bwd_preprocess": 0}
+    kern = {}
+    for name, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        fl = per_pair.get(name, 0) * pairs_step * args.steps
+        kern[name] = {"total_ms": round(ms, 3), "launches": n, "avg_launch_ms": round(ms / n, 4),
+                      "tflops": round(fl / ms / 1e9, 1) if fl else None}
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    dom_fl = per_pair[dom] * pairs_step * args.steps
+    achieved = dom_fl / kern[dom]["total_ms"] / 1e9
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
+    return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
+                roofline=roofline, flops_step=flops_step)
+
+
+# ---------------------------------------------------------------------------
+def decode_bytes(L, B, Hq, Hkv, D_, page):
+    """Algorithmic HBM bytes of one decode call: K and V rows of every live
+    position (+ the appended one), q in, out, k_new/v_new in, appended slots
+    out, and the block-table entries read."""
+    kv = sum((int(x) + 1) * Hkv * D_ * 2 * 2 for x in L)
+    small = B * Hq * D_ * 2 * 2 + B * Hkv * D_ * 2 * 2 * 2
+    bt = sum(((int(x) + 1 + page - 1) // page) * 4 for x in L)
+    return kv + small + bt
+
+
+def run_decode(args, torch, fa, splits=16):
+    from workloads import cfg5
+    dev = torch.device("cuda:0")
+    c = cfg5()
+    q, kc, vc = c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)
+    kn, vn = c.k_new.to(dev), c.v_new.to(dev)
+    sl, bt = c.cache_seqlens.to(dev), c.block_table.to(dev)
+    cos, sin = c.rotary_cos.to(dev), c.rotary_sin.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(8, 32, 1, device=dev, dtype=torch.float32)
+    res = {}
+    for ns in sorted(set([1, 4, splits])):
+        ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
+                         dtype=torch.uint8)
+
+        def call():
+            fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
+                              scale=c.scale, workspace=ws)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        fa.profiler_enable(1024)
+        fa.profiler_reset()
+        reps = max(10, args.steps * 5)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps
+        prof = fa.profiler_read()
+        fa.profiler_disable()
+        nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
+        split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
+        comb_ms = prof["decode_combine"][0] / max(1, prof["decode_combine"][1]) if prof["decode_combine"][1] else 0.0
+        res[ns] = {"num_splits": ns, "us_per_call": round(wall * 1e6, 1),
+                   "GBps": round(nbytes / wall / 1e9, 1),
+                   "split_kernel_us": round(split_ms * 1e3, 1), "combine_kernel_us": round(comb_ms * 1e3, 1),
+                   "split_kernel_GBps": round(nbytes / (split_ms * 1e-3) / 1e9, 1)}
+        log(f"decode splits={ns}: {res[ns]}")
+    best = max(res.values(), key=lambda r: r["GBps"])
+    nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
+    return {"workload": "decode bf16 B=8 Hq=32 Hkv=8 D=128 page=256 rotary128, cache_seqlens seed 5",
+            "bytes_per_call": nbytes, "best": best, "by_splits": list(res.values()),
+            "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": best["split_kernel_GBps"],
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(best["split_kernel_GBps"] / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
+# ---------------------------------------------------------------------------
+def run_cpu_baseline():
+    """The float64 oracle on a bounded sample: one (batch 0, head 0) slice of
+    the same inputs for S in {512, 1K, 2K, 4K}, non-causal and causal."""
+    import numpy as np  # noqa: F401
+    from oracle import attention_fwd, attention_bwd
+    from workloads import cfg2
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    flops, secs = 0.0, 0.0
+    for S in (512, 1024, 2048, 4096):
+        c = cfg2(S, H, D, False)
+        q, k, v, do = (t[:1, :, :1] for t in (c.q, c.k, c.v, c.dout))
+        for causal in (False, True):
+            t0 = time.perf_counter()
+            attention_fwd(q, k, v, c.scale, causal)
+            attention_bwd(q, k, v, do, c.scale, causal, check_delta=False)
+            secs += time.perf_counter() - t0
+            flops += 14 * D * (pairs_causal(S) if causal else S * S)
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "float64 numpy oracle, fwd+bwd of one (batch 0, head 0) slice of the cfg inputs for "
+                      "S in {512,1K,2K,4K}, non-causal and causal; same 14*D*pairs flop count",
+            "seconds": round(secs, 2)}
+
+
+def run_copy_calibration(torch):
+    """A plain 1 GiB device-to-device copy: FETCH_SIZE / WRITE_SIZE of this
+    dispatch against its known 1 GiB read + 1 GiB write give the counter scale."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--fwdbwd-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        run_copy_calibration(torch)
+        return
+    import io_aware_exact_qk_amd as fa
+    fa.lib()
+    if args.decode_only:
+        print(json.dumps(run_decode(args, torch, fa)))
+        return
+    fb = run_fwdbwd(args, torch, fa)
+    dec = None if args.fwdbwd_only else run_decode(args, torch, fa)
+    cpu = None if (args.no_cpu_baseline or args.fwdbwd_only) else run_cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": round(fb["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fb["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fwd+bwd bf16, hidden 2048 (H=16, D=128), B*S=16384, "
+                               "S in {512,1K,2K,4K,8K,16K}, non-causal + causal, q/k/v/dO ~ N(0,1)",
+                   "heads": H, "head_dim": D, "tokens": TOKENS, "seqlens": list(SEQLENS),
+                   "flops_per_step": fb["flops_step"]},
+        "roofline": fb["roofline"],
+        "cpu_baseline": cpu,
+        "kernels": fb["kernels"],
+        "per_config": fb["per_config"],
+        "decode": dec,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

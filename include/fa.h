@@ -1,0 +1,201 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact tiled-attention library libfa.so.
+ *
+ * The operation is standard scaled-dot-product attention computed tile by
+ * tile: Q/K/V blocks are staged on chip, QK^T feeds an online softmax that
+ * keeps a running row max and row sum, the result is multiplied into V, and
+ * the n x n score matrix is never written to memory.  The backward pass
+ * recomputes scores from the saved log-sum-exp.  (Page "FlashAttention
+ * 实战指南：如何把训练内存省 20 倍、速度提 4 倍", sections "长序列注意力为什么会爆内存"
+ * and "FlashAttention 的做法是三个手段配合"; the result equals standard
+ * attention exactly, same section.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor pointer is a DEVICE pointer unless stated otherwise,
+ *   contiguous, innermost dimension stride 1, 16-byte aligned.  The caller
+ *   allocates and frees every buffer, including workspaces; the library
+ *   keeps no per-call state and allocates no device memory.
+ * Layouts: q/out (B, Sq, Hq, D); k/v (B, Sk, Hkv, D) — the (batch, seqlen,
+ *   nheads, headdim) layout of section "上手 FlashAttention 的三步走";
+ *   lse float32 (B, Hq, Sq).  Packed varlen tensors are (total, H, D) with
+ *   lse (Hq, total_q).
+ * dtype: FA_DTYPE_FP16 or FA_DTYPE_BF16 for q/k/v/out/dout/dq/dk/dv; all
+ *   accumulation is float32.
+ * Score transform, in this order (section "进阶参数如何配置causal、window_size 与
+ *   MQA/GQA"): s = scale * q.k; softcap c > 0 gives z = c * tanh(s / c);
+ *   alibi gives z -= slope[h] * |i + Sk - Sq - j|; keys outside the window
+ *   [i' - window_left, i' + window_right] (i' = i + Sk - Sq, -1 = unbounded,
+ *   causal forces window_right = 0) are masked.  A row with no visible key
+ *   returns O = 0 and LSE = +inf.  LSE is the natural-log log-sum-exp of z.
+ * GQA/MQA: Hq must be a multiple of Hkv; query head h reads K/V head
+ *   h / (Hq / Hkv).
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = default
+ *   stream).  Calls only enqueue work; they never synchronise the device.
+ * Errors: every call validates its arguments on the host before launching
+ *   anything; on error it returns a non-zero fa_status and writes nothing.
+ *   FA_ERR_LAUNCH reports a launch failure seen by hipGetLastError.
+ * Device preconditions that are NOT checked (the data lives on the device):
+ *   cu_seqlens non-decreasing with cu[0] = 0 and cu[nseq] = total;
+ *   every block_table entry that covers a live position is a valid page;
+ *   cache capacity covers cache_seqlens[b] + Sq_new.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* a size, pointer, option or alignment is invalid */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (e.g. D = 96) */
+  FA_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than the size query */
+  FA_ERR_LAUNCH = 4       /* hipGetLastError reported an error after a launch */
+} fa_status;
+
+typedef enum { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Forward pass (section "FlashAttention 的做法是三个手段配合": tiles, online
+ * softmax; section "进阶参数如何配置…": causal, window, softcap, alibi, GQA).
+ *   q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D) in: 16-bit, read only.
+ *   out (B,Sq,Hq,D) out: 16-bit, rounded once from float32.
+ *   lse (B,Hq,Sq) out: float32; may be NULL when the caller does not need it.
+ *   D in {64, 128}; scale > 0 finite; softcap >= 0 (0 = off);
+ *   alibi_slopes: NULL or float32 (Hq,) device array, one slope per query head.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+           int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+           float scale, int causal, int window_left, int window_right, float softcap,
+           const float* alibi_slopes, void* stream);
+
+/*
+ * Backward pass: recomputes the attention weights from q, k and the saved
+ * lse instead of storing them (section "FlashAttention 的做法是三个手段配合",
+ * recomputation).  Inputs as for fa_fwd plus out, dout (B,Sq,Hq,D) and the
+ * forward's lse.  Outputs dq (B,Sq,Hq,D), dk/dv (B,Sk,Hkv,D), 16-bit,
+ * overwritten (not accumulated into).  GQA gradients are summed over the
+ * query heads of each group in a fixed order.
+ * deterministic (section "进阶参数如何配置…", deterministic=True): this
+ *   implementation never uses atomics, so every call is bitwise reproducible
+ *   whatever the flag; the flag is accepted for API compatibility.
+ * workspace: device buffer of at least fa_bwd_workspace_size(...) bytes.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+           float scale, int causal, int window_left, int window_right, float softcap,
+           const float* alibi_slopes, int deterministic,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_bwd needs (host-only, pure): a float32 row term
+ * (B, Hq, Sq) plus alignment padding. */
+size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int deterministic);
+
+/*
+ * Packed variable-length forward / backward (section "上手 FlashAttention 的三步走":
+ * batches of sequences with different lengths use the varlen interface).
+ *   q/out/dout/dq (total_q, Hq, D); k/v/dk/dv (total_k, Hkv, D); lse (Hq, total_q).
+ *   cu_seqlens_q/k: int32 device arrays (nseq + 1), prefix sums of lengths.
+ *   max_seqlen_q/k: upper bounds of the per-sequence lengths (sizes the grid).
+ * Sequence s is attention over rows [cu_q[s], cu_q[s+1]) x [cu_k[s], cu_k[s+1]),
+ * independent of every other sequence.  dk/dv rows that belong to no
+ * sequence are left untouched.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int Hq, int Hkv, int D, int dtype,
+                  float scale, int causal, int window_left, int window_right, float softcap,
+                  const float* alibi_slopes, void* stream);
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int Hq, int Hkv, int D, int dtype,
+                  float scale, int causal, int window_left, int window_right, float softcap,
+                  const float* alibi_slopes, int deterministic,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for fa_bwd_varlen: float32 (Hq, total_q) row term plus padding. */
+size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic);
+
+/*
+ * Incremental decode against a (paged) KV cache (section "增量解码场景
+ * flash_attn_with_kvcache"): the new k/v are appended to the cache in place
+ * and the new queries attend over the cache plus the appended tokens.
+ *   q (B, Sq_new, Hq, D) in; this build supports Sq_new == 1.
+ *   k_new/v_new (B, Sq_new, Hkv, D) in, or both NULL (attend without append).
+ *   k_cache/v_cache in/out: paged (n_pages, page_size, Hkv, D) when
+ *     block_table != NULL, else contiguous (B, max_blocks_per_seq*page_size, Hkv, D).
+ *   cache_seqlens: int32 (B,) valid length of each cache BEFORE the append;
+ *     never modified (the caller advances it).
+ *   block_table: int32 (B, max_blocks_per_seq); entry p of row b is the
+ *     physical page of logical positions [p*page_size, (p+1)*page_size).
+ *   page_size: a positive multiple of 32.
+ *   rotary_cos/rotary_sin: NULL or float32 (max_pos, rotary_dim/2) tables;
+ *     the half-split rotation of pairs (x_i, x_{i+rotary_dim/2}) at position
+ *     cache_seqlens[b] + t is applied to q and k_new (not to v, not to the
+ *     cached keys).  rotary_dim: multiple of 16, <= D (0 = no rotary).
+ *   out (B, Sq_new, Hq, D) out; lse (B, Hq, Sq_new) float32 out or NULL.
+ *   num_splits >= 1: the keys of each sequence are cut into num_splits
+ *     contiguous page ranges processed in parallel and merged exactly; the
+ *     result does not depend on it beyond float32 rounding.
+ *   causal: accepted; with Sq_new == 1 the new query sees every key.
+ *   window_left/right, softcap, alibi_slopes: must be -1/-1, 0 and NULL in
+ *     this build (FA_ERR_UNSUPPORTED otherwise).
+ *   workspace: fa_kvcache_workspace_size(...) bytes (0 when num_splits == 1).
+ * Appended slot (b, cache_seqlens[b] + t) receives the rotated k_new rounded
+ * once to the cache dtype and v_new unchanged; no other cache byte changes.
+ */
+int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, const int* cache_seqlens,
+                   const int* block_table, int max_blocks_per_seq, int page_size,
+                   const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                   void* out, float* lse,
+                   int B, int Sq_new, int Hq, int Hkv, int D, int dtype,
+                   float scale, int causal, int window_left, int window_right, float softcap,
+                   const float* alibi_slopes, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for fa_fwd_kvcache: float32 split partials O_s (B,Hq,Sq_new,num_splits,D)
+ * and LSE_s (B,Hq,Sq_new,num_splits), or 0 when num_splits == 1. */
+size_t fa_kvcache_workspace_size(int B, int Sq_new, int Hq, int D, int num_splits);
+
+/*
+ * Kernel timing (for benchmarks and profiles).  When enabled, every kernel
+ * the library launches is bracketed by a pair of HIP events recorded on the
+ * launch stream.  fa_profiler_read synchronises on the recorded events and
+ * returns, per kernel kind, the summed duration in milliseconds and the
+ * number of launches since the last reset.  Event pairs come from a pool
+ * created by fa_profiler_enable(1, capacity); launches past the capacity are
+ * not timed.  Host-side state, not thread safe; intended for one thread.
+ */
+typedef enum {
+  FA_KERNEL_FWD = 0,
+  FA_KERNEL_BWD_PREPROCESS = 1,
+  FA_KERNEL_BWD_DKDV = 2,
+  FA_KERNEL_BWD_DQ = 3,
+  FA_KERNEL_DECODE_SPLIT = 4,
+  FA_KERNEL_DECODE_COMBINE = 5,
+  FA_KERNEL_KIND_COUNT = 6
+} fa_kernel_kind;
+
+int fa_profiler_enable(int enable, int capacity);
+int fa_profiler_reset(void);
+int fa_profiler_read(int kind, double* total_ms, long* launches);
+const char* fa_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H_ */

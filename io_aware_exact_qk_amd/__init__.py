@@ -1,0 +1,11 @@
+"""Exact tiled attention for AMD Instinct MI355X (gfx950).
+
+The compute path is libfa.so (hand-written HIP kernels behind a C ABI,
+declared in include/fa.h); this package is its Python binding.
+"""
+from .binding import (FAError, fa_bwd, fa_bwd_varlen, fa_fwd, fa_fwd_kvcache,  # noqa: F401
+                      fa_fwd_varlen, lib, profiler_disable, profiler_enable, profiler_read,
+                      profiler_reset)
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_kvcache", "lib",
+           "FAError", "profiler_enable", "profiler_disable", "profiler_reset", "profiler_read"]

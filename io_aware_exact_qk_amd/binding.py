@@ -1,0 +1,283 @@
+"""Thin ctypes binding of libfa.so.
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, outputs are allocated with torch when the caller passes none, and the
+raw device pointers plus the current HIP stream go to the C entry points of
+the same names.  Every step of the computation runs in the library's HIP
+kernels; if the library is missing the import of this module's functions
+fails loudly — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+FA_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
+KERNEL_KINDS = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "decode_split", "decode_combine")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {lib().fa_status_string(status).decode()} (status {status})")
+
+
+def lib():
+    """Load libfa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m io_aware_exact_qk_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_status_string.argtypes = [_I]
+    L.fa_kernel_name.restype = ctypes.c_char_p
+    L.fa_kernel_name.argtypes = [_I]
+    L.fa_fwd.restype = _I
+    L.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _P]
+    L.fa_bwd.restype = _I
+    L.fa_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                         _I, _F, _P, _I, _P, _Z, _P]
+    L.fa_bwd_workspace_size.restype = _Z
+    L.fa_bwd_workspace_size.argtypes = [_I] * 7
+    L.fa_fwd_varlen.restype = _I
+    L.fa_fwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                _I, _I, _F, _P, _P]
+    L.fa_bwd_varlen.restype = _I
+    L.fa_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
+    L.fa_bwd_varlen_workspace_size.restype = _Z
+    L.fa_bwd_varlen_workspace_size.argtypes = [_I] * 4
+    L.fa_fwd_kvcache.restype = _I
+    L.fa_fwd_kvcache.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I,
+                                 _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
+    L.fa_kvcache_workspace_size.restype = _Z
+    L.fa_kvcache_workspace_size.argtypes = [_I] * 5
+    L.fa_profiler_enable.restype = _I
+    L.fa_profiler_enable.argtypes = [_I, _I]
+    L.fa_profiler_reset.restype = _I
+    L.fa_profiler_read.restype = _I
+    L.fa_profiler_read.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ utils --
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _dt(q):
+    if q.dtype not in FA_DTYPE:
+        raise ValueError(f"dtype {q.dtype} not supported (float16 / bfloat16)")
+    return FA_DTYPE[q.dtype]
+
+
+def _raise(fn, st):
+    if st != 0:
+        raise FAError(fn, st)
+
+
+def _opts(D, scale, window, softcap, alibi_slopes):
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    wl, wr = (int(window[0]), int(window[1]))
+    if alibi_slopes is not None:
+        _check(alibi_slopes, "alibi_slopes", torch.float32, 1)
+    return scale, wl, wr, float(softcap)
+
+
+# -------------------------------------------------------------- forward ----
+def fa_fwd(q, k, v, out=None, lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
+           alibi_slopes=None, stream=None):
+    """q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D) -> (out (B,Sq,Hq,D), lse (B,Hq,Sq) float32)."""
+    _check(q, "q", ndim=4)
+    _check(k, "k", q.dtype, 4)
+    _check(v, "v", q.dtype, 4)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Sk, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k/v shape mismatch")
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
+    lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, _dt(q),
+                      scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), _stream(stream))
+    _raise("fa_fwd", st)
+    return out, lse
+
+
+def fa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale=None, causal=False,
+           window=(-1, -1), softcap=0.0, alibi_slopes=None, deterministic=False, workspace=None,
+           stream=None):
+    """Gradients (dq, dk, dv) of attention given the forward's out and lse."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check(t, n, q.dtype, 4)
+    _check(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q) if dq is None else _check(dq, "dq", q.dtype)
+    dk = torch.empty_like(k) if dk is None else _check(dk, "dk", q.dtype)
+    dv = torch.empty_like(v) if dv is None else _check(dv, "dv", q.dtype)
+    L = lib()
+    ws_bytes = L.fa_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D, int(bool(deterministic)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                  _ptr(dv), B, Sq, Sk, Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc,
+                  _ptr(alibi_slopes), int(bool(deterministic)), _ptr(workspace),
+                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("fa_bwd", st)
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------- varlen ----
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out=None,
+                  lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
+                  alibi_slopes=None, stream=None):
+    """Packed q (total_q,Hq,D), k/v (total_k,Hkv,D) -> (out, lse (Hq,total_q))."""
+    _check(q, "q", ndim=3)
+    _check(k, "k", q.dtype, 3)
+    _check(v, "v", q.dtype, 3)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    tq, Hq, D = q.shape
+    tk, Hkv = k.shape[0], k.shape[1]
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q/k sizes differ")
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
+    lse = torch.empty(Hq, tq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
+                             Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc,
+                             _ptr(alibi_slopes), _stream(stream))
+    _raise("fa_fwd_varlen", st)
+    return out, lse
+
+
+def fa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  dq=None, dk=None, dv=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
+                  alibi_slopes=None, deterministic=False, workspace=None, stream=None):
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check(t, n, q.dtype, 3)
+    _check(lse, "lse", torch.float32, 2)
+    tq, Hq, D = q.shape
+    tk, Hkv = k.shape[0], k.shape[1]
+    nseq = cu_seqlens_q.numel() - 1
+    dq = torch.empty_like(q) if dq is None else _check(dq, "dq", q.dtype)
+    dk = torch.zeros_like(k) if dk is None else _check(dk, "dk", q.dtype)
+    dv = torch.zeros_like(v) if dv is None else _check(dv, "dv", q.dtype)
+    L = lib()
+    ws_bytes = L.fa_bwd_varlen_workspace_size(tq, Hq, D, int(bool(deterministic)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq,
+                         int(max_seqlen_q), int(max_seqlen_k), tq, tk, Hq, Hkv, D, _dt(q), scale,
+                         int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), int(bool(deterministic)),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("fa_bwd_varlen", st)
+    return dq, dk, dv
+
+
+# -------------------------------------------------------------- kvcache ----
+def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, block_table=None,
+                   rotary_cos=None, rotary_sin=None, rotary_dim=None, num_splits=1, out=None,
+                   lse=None, scale=None, causal=True, window=(-1, -1), softcap=0.0,
+                   alibi_slopes=None, workspace=None, stream=None):
+    """Decode step: appends k_new/v_new in place, returns (out (B,Sq,Hq,D), lse (B,Hq,Sq))."""
+    _check(q, "q", ndim=4)
+    _check(k_cache, "k_cache", q.dtype, 4)
+    _check(v_cache, "v_cache", q.dtype, 4)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, Sq, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _check(k_new, "k_new", q.dtype, 4)
+        _check(v_new, "v_new", q.dtype, 4)
+    if block_table is not None:
+        _check(block_table, "block_table", torch.int32, 2)
+        page, max_blocks = k_cache.shape[1], block_table.shape[1]
+    else:
+        page = 64 if k_cache.shape[1] % 64 == 0 else k_cache.shape[1]
+        max_blocks = k_cache.shape[1] // page
+    if rotary_cos is not None:
+        _check(rotary_cos, "rotary_cos", torch.float32, 2)
+        _check(rotary_sin, "rotary_sin", torch.float32, 2)
+        rd = 2 * rotary_cos.shape[1] if rotary_dim is None else int(rotary_dim)
+    else:
+        rd = 0
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
+    lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    L = lib()
+    ws_bytes = L.fa_kvcache_workspace_size(B, Sq, Hq, D, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_fwd_kvcache(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(cache_seqlens), _ptr(block_table), max_blocks, page, _ptr(rotary_cos),
+                          _ptr(rotary_sin), rd, _ptr(out), _ptr(lse), B, Sq, Hq, Hkv, D, _dt(q), scale,
+                          int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), int(num_splits),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("fa_fwd_kvcache", st)
+    return out, lse
+
+
+# ------------------------------------------------------------- profiler ----
+def profiler_enable(capacity=4096):
+    _raise("fa_profiler_enable", lib().fa_profiler_enable(1, int(capacity)))
+
+
+def profiler_disable():
+    _raise("fa_profiler_enable", lib().fa_profiler_enable(0, 0))
+
+
+def profiler_reset():
+    _raise("fa_profiler_reset", lib().fa_profiler_reset())
+
+
+def profiler_read():
+    """{kernel name: (total_ms, launches)} since the last reset (synchronises)."""
+    res = {}
+    for i, name in enumerate(KERNEL_KINDS):
+        ms, n = ctypes.c_double(0), ctypes.c_long(0)
+        _raise("fa_profiler_read", lib().fa_profiler_read(i, ctypes.byref(ms), ctypes.byref(n)))
+        res[name] = (ms.value, n.value)
+    return res

@@ -1,0 +1,614 @@
+// fa_bwd.hip — backward pass of exact tiled attention on gfx950.
+//
+// The attention weights are not stored by the forward pass; they are
+// recomputed here from q, k and the saved log-sum-exp (page "FlashAttention
+// 实战指南：如何把训练内存省 20 倍、速度提 4 倍", section "FlashAttention 的做法是三个手段配合":
+// recomputation is cheaper than round trips through HBM).  With z the final
+// logits, P = exp(z - LSE) and
+//   dV = P^T dO,  dP = dO V^T,  dZ = P * (dP - rowsum(dO * O)),
+//   dS = dZ * (1 - tanh^2(s/c)) with softcap c (else dZ),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels, none with atomics, so every result is bitwise reproducible
+// (the pages' deterministic=True option is therefore always satisfied):
+//   1. row term  delta_i = sum_d dO_id O_id  (float32);
+//   2. dK/dV: one work-group per 128 keys of one K/V head; each wave keeps 32
+//      keys' K and V rows in VGPRs and walks every query head of its group and
+//      every query tile of 32 rows in a fixed order, with Q and dO tiles
+//      staged in LDS.  S = Q K^T puts one key per lane, so dV^T += dO^T P and
+//      dK^T += Q^T dS take P / dS straight from the accumulators;
+//   3. dQ: one work-group per 128 query rows of one query head (same layout
+//      as the forward); it recomputes S^T and dP^T per key tile and
+//      accumulates dQ^T += K^T dS^T.
+#include "fa_device.h"
+#include "fa_host.h"
+
+namespace fa {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  float* dvec;  // workspace: row term, same layout as lse
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int* cu_q;
+  const int* cu_k;
+  int Sq, Sk, Hq, g, total_q;
+  int q_rstride, k_rstride;
+  float scale, scale_log2, scale_over_cap, cap_log2;
+  const float* alibi;
+  int wl, wr;
+  int n_tiles, n_heads, n_batch, reverse;
+  int n_tokens;  // preprocess: number of (token) rows
+};
+
+struct SeqBounds {
+  int q_start, Sq, k_start, Sk;
+};
+
+__device__ __forceinline__ SeqBounds seq_bounds(const BwdParams& p, int b) {
+  SeqBounds s;
+  if (p.cu_q) {
+    s.q_start = p.cu_q[b];
+    s.Sq = p.cu_q[b + 1] - s.q_start;
+    s.k_start = p.cu_k[b];
+    s.Sk = p.cu_k[b + 1] - s.k_start;
+  } else {
+    s.q_start = b * p.Sq;
+    s.Sq = p.Sq;
+    s.k_start = b * p.Sk;
+    s.Sk = p.Sk;
+  }
+  return s;
+}
+
+__device__ __forceinline__ int64_t row_index(const BwdParams& p, int b, int h, int q_start, int Sq, int i) {
+  return p.cu_q ? (int64_t)h * p.total_q + q_start + i : ((int64_t)b * p.Hq + h) * Sq + i;
+}
+
+// ------------------------------------------------------------ row term ----
+// One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int NCH = D / 8;
+  const int gid = (blockIdx.x * 256 + threadIdx.x) / NCH;
+  const int ch = threadIdx.x % NCH;
+  const int token = gid / p.Hq, h = gid % p.Hq;
+  const bool ok = token < p.n_tokens;
+  float acc = 0.0f;
+  if (ok) {
+    const int64_t base = (int64_t)token * p.q_rstride + h * D + ch * 8;
+    const u32x4 a = gload128(p.o + base);
+    const u32x4 c = gload128(p.dout + base);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(to_f32<DT>((uint16_t)(a[e] & 0xffff)), to_f32<DT>((uint16_t)(c[e] & 0xffff)), acc);
+      acc = fmaf(to_f32<DT>((uint16_t)(a[e] >> 16)), to_f32<DT>((uint16_t)(c[e] >> 16)), acc);
+    }
+  }
+#pragma unroll
+  for (int m = NCH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (ok && ch == 0) {
+    int64_t idx;
+    if (p.cu_q) {
+      idx = (int64_t)h * p.total_q + token;
+    } else {
+      const int b = token / p.Sq, i = token % p.Sq;
+      idx = ((int64_t)b * p.Hq + h) * p.Sq + i;
+    }
+    p.dvec[idx] = acc;
+  }
+}
+
+// --------------------------------------------------- logit transform ------
+// Log2-domain logit x of raw dot product s for query position ip, key j;
+// also returns t = tanh(s * scale / c) for the softcap derivative.
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float logit2(float s, int ip, int j, const BwdParams& p, float slope_log2, float& t) {
+  float x;
+  if constexpr (SOFTCAP) {
+    t = tanh_exp(s * p.scale_over_cap);
+    x = p.cap_log2 * t;
+  } else {
+    t = 0.0f;
+    x = s * p.scale_log2;
+  }
+  if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
+  return x;
+}
+
+// --------------------------------------------------------------- dK / dV --
+template <int D, int DT, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BC = 128, BR = 32;
+  constexpr int NCH = D / 8, KC = D / 16, DB = D / 32;
+  constexpr int TILE = BR * D * 2;
+  constexpr int RPP = 256 / NCH;
+  constexpr int PASSES = (BR + RPP - 1) / RPP;
+  constexpr int STAGE = 2 * TILE + 2 * BR * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, r = lane & 31;
+  const int nwg = p.n_tiles * p.n_heads * p.n_batch;
+  const int id = xcd_remap((int)blockIdx.x, nwg);
+  const int tk = id % p.n_tiles;
+  const int hk = (id / p.n_tiles) % p.n_heads;
+  const int b = id / (p.n_tiles * p.n_heads);
+  const SeqBounds sb = seq_bounds(p, b);
+  const int k0 = tk * BC;
+  if (k0 >= sb.Sk) return;
+  const int Sq = sb.Sq, Sk = sb.Sk, off = Sk - Sq;
+  const MaskSpec mask{p.wl, p.wr};
+
+  const int kw0 = k0 + 32 * w;
+  const int my_key = kw0 + r;
+  const bool key_ok = my_key < Sk;
+  const int64_t krow = (int64_t)(sb.k_start + my_key) * p.k_rstride + hk * D;
+
+  u32x4 kreg[KC], vreg[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    kreg[c] = key_ok ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    vreg[c] = key_ok ? gload128(p.v + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+  }
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    dkacc[d] = f32x16{};
+    dvacc[d] = f32x16{};
+  }
+
+  // query rows that can see any key of this work-group
+  const int k1 = min(k0 + BC, Sk) - 1;
+  int i_lo = 0, i_hi = Sq;
+  if (p.wr >= 0) i_lo = max(0, k0 - p.wr - off);
+  if (p.wl >= 0) i_hi = min(Sq, k1 + p.wl - off + 1);
+  if (i_lo < i_hi && Sq > 0) {
+    const int t_lo = i_lo / BR, nt = (i_hi + BR - 1) / BR - t_lo;
+    const int n_iter = nt * p.g;
+    const int lrow = tid / NCH, lch = tid % NCH;
+    u32x4 qpre[PASSES], dopre[PASSES];
+    float lpre = 0.0f, dpre = 0.0f;
+    auto load = [&](int n) {
+      const int hq = hk * p.g + n / nt;
+      const int i0 = (t_lo + n % nt) * BR;
+      const int64_t hoff = (int64_t)hq * D;
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = lrow + it * RPP;
+        const int i = i0 + row;
+        if (row < BR && i < Sq) {
+          const int64_t a = (int64_t)(sb.q_start + i) * p.q_rstride + hoff + lch * 8;
+          qpre[it] = gload128(p.q + a);
+          dopre[it] = gload128(p.dout + a);
+        } else {
+          qpre[it] = u32x4{0, 0, 0, 0};
+          dopre[it] = u32x4{0, 0, 0, 0};
+        }
+      }
+      if (tid < BR) {
+        const int i = i0 + tid;
+        if (i < Sq) {
+          const int64_t ri = row_index(p, b, hq, sb.q_start, Sq, i);
+          lpre = p.lse[ri] * kLog2e;
+          dpre = p.dvec[ri];
+        } else {
+          lpre = INFINITY;
+          dpre = 0.0f;
+        }
+      }
+    };
+    auto store = [&](int buf) {
+      char* st = smem + buf * STAGE;
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = lrow + it * RPP;
+        if (row < BR) {
+          const uint32_t o = tile_off<D>(row, lch);
+          lds_write128(st, o, qpre[it]);
+          lds_write128(st + TILE, o, dopre[it]);
+        }
+      }
+      if (tid < BR) {
+        reinterpret_cast<float*>(st + 2 * TILE)[tid] = lpre;
+        reinterpret_cast<float*>(st + 2 * TILE + BR * 4)[tid] = dpre;
+      }
+    };
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int n = 0; n < n_iter; ++n) {
+      const int buf = n & 1;
+      const bool more = n + 1 < n_iter;
+      if (more) load(n + 1);
+      const int hq = hk * p.g + n / nt;
+      const int i0 = (t_lo + n % nt) * BR;
+      const char* st = smem + buf * STAGE;
+      const char* qt = st;
+      const char* dot = st + TILE;
+      const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
+      const float* dvs = lse2 + BR;
+      const int i1 = min(i0 + BR - 1, Sq - 1);
+      const int cls = classify(i0 + off, i1 + off, kw0, kw0 + 31, Sk, mask);
+      if (cls != 0) {
+        const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
+        // S = Q K^T and dP = dO V^T: rows = 32 queries, columns = this wave's keys
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          s = mfma32<DT>(lds_read_nat<D>(qt, r, 2 * c + g), kreg[c], s);
+          dp = mfma32<DT>(lds_read_nat<D>(dot, r, 2 * c + g), vreg[c], dp);
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * qd + 4 * g);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvs + 8 * qd + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ii = 4 * qd + e;
+            const int row = i0 + frag_row(ii, g);
+            const int ip = row + off;
+            float t;
+            const float x = logit2<SOFTCAP, ALIBI>(s[ii], ip, my_key, p, slope_log2, t);
+            float pv = fast_exp2(x - l4[e]);
+            if (cls == 1 && !(key_ok && visible(ip, my_key, Sk, mask))) pv = 0.0f;
+            float ds = pv * (dp[ii] - d4[e]);
+            if constexpr (SOFTCAP) ds *= (1.0f - t * t);
+            s[ii] = pv;
+            dp[ii] = ds;
+          }
+        }
+        // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over the 32 query rows)
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk) {
+          const u32x4 pb = pack_frag_half<DT>(s, mk);
+          const u32x4 sb2 = pack_frag_half<DT>(dp, mk);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            dvacc[d] = mfma32<DT>(lds_read_At<D>(dot, 16 * mk, 32 * d, lane), pb, dvacc[d]);
+            dkacc[d] = mfma32<DT>(lds_read_At<D>(qt, 16 * mk, 32 * d, lane), sb2, dkacc[d]);
+          }
+        }
+      }
+      if (more) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (key_ok) {
+    uint16_t* dkrow = p.dk + krow;
+    uint16_t* dvrow = p.dv + krow;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 a, c;
+        a[0] = pack2<DT>(dkacc[d][4 * qd + 0] * p.scale, dkacc[d][4 * qd + 1] * p.scale);
+        a[1] = pack2<DT>(dkacc[d][4 * qd + 2] * p.scale, dkacc[d][4 * qd + 3] * p.scale);
+        c[0] = pack2<DT>(dvacc[d][4 * qd + 0], dvacc[d][4 * qd + 1]);
+        c[1] = pack2<DT>(dvacc[d][4 * qd + 2], dvacc[d][4 * qd + 3]);
+        gstore64(dkrow + 32 * d + 8 * qd + 4 * g, a);
+        gstore64(dvrow + 32 * d + 8 * qd + 4 * g, c);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ ----
+template <int D, int DT, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int NCH = D / 8, KC = D / 16, DB = D / 32;
+  constexpr int TILE = BC * D * 2;
+  constexpr int RPP = 256 / NCH;
+  constexpr int PASSES = BC / RPP;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, r = lane & 31;
+  const int nwg = p.n_tiles * p.n_heads * p.n_batch;
+  const int id = xcd_remap((int)blockIdx.x, nwg);
+  int tq = id % p.n_tiles;
+  const int h = (id / p.n_tiles) % p.n_heads;
+  const int b = id / (p.n_tiles * p.n_heads);
+  if (p.reverse) tq = p.n_tiles - 1 - tq;
+  const SeqBounds sb = seq_bounds(p, b);
+  const int q0 = tq * BR;
+  if (q0 >= sb.Sq) return;
+  const int Sq = sb.Sq, Sk = sb.Sk, off = Sk - Sq;
+  const int hk = h / p.g;
+  const MaskSpec mask{p.wl, p.wr};
+
+  const int wrow0 = q0 + 32 * w;
+  const int wrow1 = min(wrow0 + 31, Sq - 1);
+  const int my_row = wrow0 + r;
+  const bool row_ok = my_row < Sq;
+  const int ip = my_row + off;
+  const int64_t qrow = (int64_t)(sb.q_start + my_row) * p.q_rstride + h * D;
+
+  u32x4 qreg[KC], doreg[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qreg[c] = row_ok ? gload128(p.q + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    doreg[c] = row_ok ? gload128(p.dout + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+  }
+  float lse2 = INFINITY, dv_row = 0.0f;
+  if (row_ok) {
+    const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
+    lse2 = p.lse[ri] * kLog2e;
+    dv_row = p.dvec[ri];
+  }
+  const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) dqacc[d] = f32x16{};
+
+  const int qend = min(q0 + BR, Sq);
+  int kv_lo = 0, kv_hi = Sk;
+  if (p.wl >= 0) kv_lo = max(0, q0 + off - p.wl);
+  if (p.wr >= 0) kv_hi = min(Sk, qend - 1 + off + p.wr + 1);
+  const uint16_t* kbase = p.k + (int64_t)sb.k_start * p.k_rstride + hk * D;
+  const uint16_t* vbase = p.v + (int64_t)sb.k_start * p.k_rstride + hk * D;
+
+  if (kv_lo < kv_hi) {
+    const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+    const int lrow = tid / NCH, lch = tid % NCH;
+    u32x4 kpre[PASSES], vpre[PASSES];
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int j = t * BC + lrow + it * RPP;
+        if (j < Sk) {
+          kpre[it] = gload128(kbase + (int64_t)j * p.k_rstride + lch * 8);
+          vpre[it] = gload128(vbase + (int64_t)j * p.k_rstride + lch * 8);
+        } else {
+          kpre[it] = u32x4{0, 0, 0, 0};
+          vpre[it] = u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto store_tile = [&](int buf) {
+      char* kt = smem + buf * 2 * TILE;
+      char* vt = kt + TILE;
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const uint32_t o = tile_off<D>(lrow + it * RPP, lch);
+        lds_write128(kt, o, kpre[it]);
+        lds_write128(vt, o, vpre[it]);
+      }
+    };
+    load_tile(t_lo);
+    store_tile(0);
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; ++t) {
+      const int buf = (t - t_lo) & 1;
+      const bool more = t + 1 < t_hi;
+      if (more) load_tile(t + 1);
+      const char* kt = smem + buf * 2 * TILE;
+      const char* vt = kt + TILE;
+      const int j0 = t * BC;
+      const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
+      if (cls != 0) {
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+          dp[kb] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            s[kb] = mfma32<DT>(lds_read_nat<D>(kt, kb * 32 + r, 2 * c + g), qreg[c], s[kb]);
+            dp[kb] = mfma32<DT>(lds_read_nat<D>(vt, kb * 32 + r, 2 * c + g), doreg[c], dp[kb]);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * kb + frag_row(i, g);
+            float t;
+            const float x = logit2<SOFTCAP, ALIBI>(s[kb][i], ip, j, p, slope_log2, t);
+            float pv = fast_exp2(x - lse2);
+            if (cls == 1 && !(row_ok && visible(ip, j, Sk, mask))) pv = 0.0f;
+            float ds = pv * (dp[kb][i] - dv_row);
+            if constexpr (SOFTCAP) ds *= (1.0f - t * t);
+            dp[kb][i] = ds;
+          }
+        }
+        // dQ^T += K^T dS^T  (contraction over the 64 keys)
+#pragma unroll
+        for (int mk = 0; mk < 4; ++mk) {
+          const u32x4 db = pack_frag_half<DT>(dp[mk >> 1], mk & 1);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            dqacc[d] = mfma32<DT>(lds_read_At<D>(kt, 16 * mk, 32 * d, lane), db, dqacc[d]);
+          }
+        }
+      }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (row_ok) {
+    uint16_t* drow = p.dq + qrow;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 v2;
+        v2[0] = pack2<DT>(dqacc[d][4 * qd + 0] * p.scale, dqacc[d][4 * qd + 1] * p.scale);
+        v2[1] = pack2<DT>(dqacc[d][4 * qd + 2] * p.scale, dqacc[d][4 * qd + 3] * p.scale);
+        gstore64(drow + 32 * d + 8 * qd + 4 * g, v2);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- dispatch ---
+template <int D, int DT, bool SC, bool AL>
+static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
+  if (nwg_kv > 0) {
+    prof_before(FA_KERNEL_BWD_DKDV, st);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL>), dim3(nwg_kv), dim3(256), 0, st, dkdv);
+    prof_after(FA_KERNEL_BWD_DKDV, st);
+  }
+  if (nwg_q > 0) {
+    prof_before(FA_KERNEL_BWD_DQ, st);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL>), dim3(nwg_q), dim3(256), 0, st, dq);
+    prof_after(FA_KERNEL_BWD_DQ, st);
+  }
+}
+
+template <int D, int DT>
+static void launch_all(const BwdParams& pre, int nwg_pre, const BwdParams& dkdv, const BwdParams& dq,
+                       int nwg_kv, int nwg_q, bool sc, bool al, hipStream_t st) {
+  if (nwg_pre > 0) {
+    prof_before(FA_KERNEL_BWD_PREPROCESS, st);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3(nwg_pre), dim3(256), 0, st, pre);
+    prof_after(FA_KERNEL_BWD_PREPROCESS, st);
+  }
+  if (sc) {
+    if (al) launch_main<D, DT, true, true>(dkdv, dq, nwg_kv, nwg_q, st);
+    else launch_main<D, DT, true, false>(dkdv, dq, nwg_kv, nwg_q, st);
+  } else {
+    if (al) launch_main<D, DT, false, true>(dkdv, dq, nwg_kv, nwg_q, st);
+    else launch_main<D, DT, false, false>(dkdv, dq, nwg_kv, nwg_q, st);
+  }
+}
+
+static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int max_sk, int nbatch,
+                   int n_tokens, int causal, hipStream_t st) {
+  if (causal) base.wr = 0;
+  BwdParams pre = base;
+  pre.n_tokens = n_tokens;
+  const long long pre_threads = (long long)n_tokens * base.Hq * (D / 8);
+  const long long nwg_pre = (pre_threads + 255) / 256;
+  BwdParams kv = base;
+  kv.n_tiles = (max_sk + 127) / 128;
+  kv.n_heads = Hkv;
+  kv.n_batch = nbatch;
+  kv.reverse = 0;
+  BwdParams dq = base;
+  dq.n_tiles = (max_sq + 127) / 128;
+  dq.n_heads = base.Hq;
+  dq.n_batch = nbatch;
+  dq.reverse = causal ? 1 : 0;
+  const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * nbatch;
+  const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * nbatch;
+  if (nwg_pre > 0x7fffffffLL || nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  const bool sc = base.cap_log2 > 0.0f, al = base.alibi != nullptr;
+  if (D == 128) {
+    if (dtype == FA_DTYPE_BF16) launch_all<128, DT_BF16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
+    else launch_all<128, DT_F16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
+  } else {
+    if (dtype == FA_DTYPE_BF16) launch_all<64, DT_BF16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
+    else launch_all<64, DT_F16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
+  }
+  return launch_status();
+}
+
+static void fill_common(BwdParams& p, const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int Hq, int Hkv,
+                        int D, float scale, int wl, int wr, float softcap, const float* alibi) {
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)out;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.Hq = Hq;
+  p.g = Hq / Hkv;
+  p.q_rstride = Hq * D;
+  p.k_rstride = Hkv * D;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  p.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
+  p.cap_log2 = softcap * kLog2e;
+  p.alibi = alibi;
+  p.wl = wl;
+  p.wr = wr;
+}
+
+static bool bwd_ptrs_ok(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, const float* alibi) {
+  return aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(dout) &&
+         aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned4(lse) && (!alibi || aligned4(alibi));
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int deterministic) {
+  (void)Sk;
+  (void)Hkv;
+  (void)D;
+  (void)deterministic;
+  if (B < 1 || Sq < 1 || Hq < 1) return 0;
+  return align_up((size_t)B * Hq * Sq * sizeof(float), 256);
+}
+
+extern "C" size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic) {
+  (void)D;
+  (void)deterministic;
+  if (total_q < 0 || Hq < 1) return 0;
+  return align_up((size_t)total_q * Hq * sizeof(float), 256);
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, int deterministic,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
+  if (st) return st;
+  if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
+  if (!bwd_ptrs_ok(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D, deterministic);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  BwdParams p{};
+  fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
+              alibi_slopes);
+  p.dvec = (float*)workspace;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, B * Sq, causal, (hipStream_t)stream);
+}
+
+extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                             int Hq, int Hkv, int D, int dtype,
+                             float scale, int causal, int window_left, int window_right, float softcap,
+                             const float* alibi_slopes, int deterministic,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
+  if (st) return st;
+  if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return FA_ERR_INVALID_ARG;
+  if (!bwd_ptrs_ok(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_varlen_workspace_size(total_q, Hq, D, deterministic);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if (total_q == 0 || total_k == 0) return FA_OK;
+  BwdParams p{};
+  fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
+              alibi_slopes);
+  p.dvec = (float*)workspace;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, total_q, causal, (hipStream_t)stream);
+}

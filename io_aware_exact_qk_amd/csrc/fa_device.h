@@ -1,0 +1,188 @@
+// fa_device.h — CDNA4 (gfx950) building blocks shared by the attention kernels.
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_{bf16,f16}, one wave of 64 lanes):
+//   lane l, g = l / 32 (0 or 1), r = l % 32.
+//   A operand (32 x 16): lane l holds row r, 8 contraction elements.
+//   B operand (16 x 32): lane l holds column r, 8 contraction elements.
+//   C/D (32 x 32 f32):   lane l holds column r, element i at row
+//                        8*(i/4) + 4*g + (i%4).
+// Which contraction index each (g, element) pair stands for is up to the
+// caller as long as A and B agree.  Two assignments are used here:
+//   * "natural":   element e of group g is k = 8*g + e within a 16-wide chunk,
+//                  i.e. 16 contiguous bytes of a row (one ds_read_b128);
+//   * "acc-order": element e of group g is k = 8*(e/4) + 4*g + (e%4), which is
+//                  exactly the row order of a C fragment, so 8 consecutive
+//                  accumulator elements of a fragment can be fed back as a B
+//                  operand without moving data between lanes.
+// A operands whose contraction runs along LDS rows (V^T, K^T, Q^T, dO^T) are
+// read in acc-order with ds_read_b64_tr_b16: within each 16-lane group the
+// four 8-byte fetches of lanes 4r..4r+3 form row r of a 4x16 tile and lane i
+// receives column i of that tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- MFMA ----
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// Two float32 -> one dword of two 16-bit values, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  if constexpr (DT == DT_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+}
+
+// Elements 8*half .. 8*half+7 of an accumulator fragment, rounded to 16 bits
+// and packed as a B operand in acc-order.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_frag_half(const f32x16& c, int half) {
+  u32x4 r;
+  const int o = 8 * half;
+  r[0] = pack2<DT>(c[o + 0], c[o + 1]);
+  r[1] = pack2<DT>(c[o + 2], c[o + 3]);
+  r[2] = pack2<DT>(c[o + 4], c[o + 5]);
+  r[3] = pack2<DT>(c[o + 6], c[o + 7]);
+  return r;
+}
+
+// Row of element i of a C fragment held by a lane of group g.
+__device__ __forceinline__ int frag_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// ------------------------------------------------------------- LDS tiles --
+// A tile is ROWS x D 16-bit elements stored row-major; its 16-byte chunks are
+// permuted within each row by an XOR so that
+//  * 8 consecutive rows read at the same logical chunk (ds_read_b128, A/B
+//    operands in natural order) touch 8 different bank groups, and
+//  * the 4 rows x 2 chunks fetched by one 16-lane group of a transposed read
+//    touch 8 different bank groups.
+__device__ __forceinline__ uint32_t swz(int row) { return (uint32_t)(((row & 3) << 1) | ((row >> 2) & 1)); }
+
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)row * (D * 2) + (((uint32_t)chunk ^ swz(row)) << 4);
+}
+
+// Byte offset of element (row, col) where col is a multiple of 4.
+template <int D>
+__device__ __forceinline__ uint32_t tile_off_elem4(int row, int col) {
+  return tile_off<D>(row, col >> 3) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x4 lds_read128(const char* smem, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(smem + off);
+}
+
+__device__ __forceinline__ void lds_write128(char* smem, uint32_t off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(smem + off) = v;
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr(const char* smem, uint32_t off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A operand (32 x 16) whose 32 rows are tile columns col0 .. col0+31 and whose
+// contraction runs over tile rows row0 .. row0+15 in acc-order.
+template <int D>
+__device__ __forceinline__ u32x4 lds_read_At(const char* smem, int row0, int col0, int lane) {
+  const int grp = lane >> 4;        // 16-lane group 0..3
+  const int i = lane & 15;
+  const int g = grp >> 1;           // which half of the wave (acc-order group)
+  const int col = col0 + 16 * (grp & 1) + 4 * (i & 3);
+  const int r = row0 + 4 * g + (i >> 2);
+  u32x2 lo = lds_read_tr(smem, tile_off_elem4<D>(r, col));
+  u32x2 hi = lds_read_tr(smem, tile_off_elem4<D>(r + 8, col));
+  u32x4 out = {lo[0], lo[1], hi[0], hi[1]};
+  return out;
+}
+
+// Natural-order operand: 8 contiguous elements of tile row `row`, chunk `chunk`.
+template <int D>
+__device__ __forceinline__ u32x4 lds_read_nat(const char* smem, int row, int chunk) {
+  return lds_read128(smem, tile_off<D>(row, chunk));
+}
+
+// ------------------------------------------------------------ wave utils --
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh from the identity tanh(y) = 1 - 2 / (1 + e^{2y}); its absolute error is
+// a few float32 ulps of 1 for every y (e^{2y} overflowing to +inf gives 1,
+// underflowing to 0 gives -1).
+__device__ __forceinline__ float tanh_exp(float y) {
+  const float e = fast_exp2(y * (2.0f * kLog2e));
+  return 1.0f - 2.0f * fast_rcp(1.0f + e);
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 gload128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void gstore128(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void gstore64(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// ---------------------------------------------------------- mask logic ----
+// Visibility of key j to query row i (aligned position ip = i + Sk - Sq):
+//   j < Sk, j >= ip - wl (wl >= 0), j <= ip + wr (wr >= 0).  Causal is folded
+// into wr = 0 by the host.
+struct MaskSpec {
+  int wl, wr;  // -1 = unbounded
+};
+
+__device__ __forceinline__ bool visible(int ip, int j, int Sk, MaskSpec m) {
+  return j < Sk && (m.wl < 0 || j >= ip - m.wl) && (m.wr < 0 || j <= ip + m.wr);
+}
+
+// Block-level classification for query positions [ip0, ip1] and keys [j0, j1].
+// Returns 0 = nothing visible, 1 = partially visible, 2 = everything visible.
+__device__ __forceinline__ int classify(int ip0, int ip1, int j0, int j1, int Sk, MaskSpec m) {
+  if (j0 >= Sk) return 0;
+  if (m.wr >= 0 && j0 > ip1 + m.wr) return 0;
+  if (m.wl >= 0 && j1 < ip0 - m.wl) return 0;
+  const bool full = (j1 < Sk) && (m.wr < 0 || j1 <= ip0 + m.wr) && (m.wl < 0 || j0 >= ip1 - m.wl);
+  return full ? 2 : 1;
+}
+
+}  // namespace fa

@@ -1,0 +1,346 @@
+// fa_fwd.hip — forward pass of exact tiled attention on gfx950.
+//
+// Method (page "FlashAttention 实战指南：如何把训练内存省 20 倍、速度提 4 倍", section
+// "FlashAttention 的做法是三个手段配合"): Q, K, V are cut into blocks, the current
+// block is staged on chip, QK^T and the softmax of that block are done there,
+// and an online softmax updates a running row maximum and row sum block by
+// block, so the n x n matrix never exists in memory.
+//
+// Work decomposition (one work-group = 4 waves = 128 query rows of one head):
+//   * each wave owns 32 query rows; their Q fragment stays in VGPRs for the
+//     whole key loop (B operand of S^T = K Q^T);
+//   * K and V tiles of 64 keys are streamed HBM -> VGPR -> LDS, double
+//     buffered, so the next tile's loads overlap this tile's matrix work;
+//   * S^T = K Q^T on MFMA 32x32x16 puts one query per lane (two lanes per
+//     query, 16 keys each), so the row max needs one cross-lane step and the
+//     row sum none until the epilogue;
+//   * O^T += V^T P^T: P^T is fed back from the S^T accumulator registers in
+//     acc-order and V^T is read from the row-major V tile with transposing
+//     LDS reads;
+//   * the online softmax works in the log2 domain: p = exp2(x - m).
+#include "fa_device.h"
+#include "fa_host.h"
+
+namespace fa {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int* cu_q;  // packed layout when non-null
+  const int* cu_k;
+  int Sq, Sk;       // per-batch lengths (dense layout)
+  int Hq, g;        // query heads, query heads per K/V head
+  int total_q;      // packed layout: LSE row stride
+  int q_rstride;    // elements between consecutive tokens of q/o (Hq * D)
+  int k_rstride;    // elements between consecutive tokens of k/v (Hkv * D)
+  float scale_log2;     // scale * log2(e)
+  float scale_over_cap; // scale / softcap
+  float cap_log2;       // softcap * log2(e)
+  const float* alibi;
+  int wl, wr;           // window, causal folded into wr = 0
+  int n_qtiles, n_heads, n_batch;
+  int reverse;          // causal: heaviest tiles first
+};
+
+template <int D, int DT, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int NCH = D / 8;               // 16-byte chunks per row
+  constexpr int KC = D / 16;               // MFMA steps along D
+  constexpr int DB = D / 32;               // 32-wide output blocks along D
+  constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
+  constexpr int RPP = 256 / NCH;           // rows per load pass
+  constexpr int PASSES = BC / RPP;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, r = lane & 31;
+
+  // logical tile id -> (q tile, head, batch)
+  const int nwg = p.n_qtiles * p.n_heads * p.n_batch;
+  const int id = xcd_remap((int)blockIdx.x, nwg);
+  int tq = id % p.n_qtiles;
+  const int h = (id / p.n_qtiles) % p.n_heads;
+  const int b = id / (p.n_qtiles * p.n_heads);
+  if (p.reverse) tq = p.n_qtiles - 1 - tq;
+
+  int q_start, Sq, k_start, Sk;
+  if (p.cu_q) {
+    q_start = p.cu_q[b];
+    Sq = p.cu_q[b + 1] - q_start;
+    k_start = p.cu_k[b];
+    Sk = p.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * p.Sq;
+    Sq = p.Sq;
+    k_start = b * p.Sk;
+    Sk = p.Sk;
+  }
+  const int q0 = tq * BR;
+  if (q0 >= Sq) return;  // uniform over the work-group
+  const int hk = h / p.g;
+  const int off = Sk - Sq;
+  const MaskSpec mask{p.wl, p.wr};
+
+  const uint16_t* qbase = p.q + (int64_t)q_start * p.q_rstride + h * D;
+  const uint16_t* kbase = p.k + (int64_t)k_start * p.k_rstride + hk * D;
+  const uint16_t* vbase = p.v + (int64_t)k_start * p.k_rstride + hk * D;
+
+  const int qend = min(q0 + BR, Sq);
+  int kv_lo = 0, kv_hi = Sk;
+  if (p.wl >= 0) kv_lo = max(0, q0 + off - p.wl);
+  if (p.wr >= 0) kv_hi = min(Sk, qend - 1 + off + p.wr + 1);
+
+  const int wrow0 = q0 + 32 * w;
+  const int wrow1 = min(wrow0 + 31, Sq - 1);
+  const int my_row = wrow0 + r;
+  const bool row_ok = my_row < Sq;
+  const int ip = my_row + off;
+
+  u32x4 qreg[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qreg[c] = row_ok ? gload128(qbase + (int64_t)my_row * p.q_rstride + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
+  const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
+
+  if (kv_lo < kv_hi) {
+    const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+    const int lrow = tid / NCH, lch = tid % NCH;
+    u32x4 kpre[PASSES], vpre[PASSES];
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int j = t * BC + lrow + it * RPP;
+        if (j < Sk) {
+          kpre[it] = gload128(kbase + (int64_t)j * p.k_rstride + lch * 8);
+          vpre[it] = gload128(vbase + (int64_t)j * p.k_rstride + lch * 8);
+        } else {
+          kpre[it] = u32x4{0, 0, 0, 0};
+          vpre[it] = u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto store_tile = [&](int buf) {
+      char* kt = smem + buf * 2 * TILE;
+      char* vt = kt + TILE;
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const uint32_t o = tile_off<D>(lrow + it * RPP, lch);
+        lds_write128(kt, o, kpre[it]);
+        lds_write128(vt, o, vpre[it]);
+      }
+    };
+
+    load_tile(t_lo);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = t_lo; t < t_hi; ++t) {
+      const int buf = (t - t_lo) & 1;
+      const bool more = t + 1 < t_hi;
+      if (more) load_tile(t + 1);
+      const char* kt = smem + buf * 2 * TILE;
+      const char* vt = kt + TILE;
+      const int j0 = t * BC;
+      const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
+      if (cls != 0) {
+        // ---- S^T = K Q^T for 64 keys x 32 queries ----
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            s[kb] = mfma32<DT>(lds_read_nat<D>(kt, kb * 32 + r, 2 * c + g), qreg[c], s[kb]);
+          }
+        }
+        // ---- score transform and mask ----
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = s[kb][i];
+            const int j = j0 + 32 * kb + frag_row(i, g);
+            if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
+            else if constexpr (ALIBI) x = x * p.scale_log2;
+            if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
+            if (cls == 1 && !(row_ok && visible(ip, j, Sk, mask))) x = -INFINITY;
+            s[kb][i] = x;
+          }
+        }
+        // ---- online softmax (log2 domain) ----
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_run, mx * fs);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = fast_exp2(fmaf(s[kb][i], fs, -m_use));
+            s[kb][i] = pv;
+            lsum += pv;
+          }
+        l_run = fmaf(l_run, alpha, lsum);
+        m_run = m_new;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+        }
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int mk = 0; mk < 4; ++mk) {
+          const u32x4 pb = pack_frag_half<DT>(s[mk >> 1], mk & 1);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            oacc[d] = mfma32<DT>(lds_read_At<D>(vt, 16 * mk, 32 * d, lane), pb, oacc[d]);
+          }
+        }
+      }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  const float l_tot = l_run + xor32(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.q_rstride + h * D;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 v2;
+        v2[0] = pack2<DT>(oacc[d][4 * qd + 0] * inv, oacc[d][4 * qd + 1] * inv);
+        v2[1] = pack2<DT>(oacc[d][4 * qd + 2] * inv, oacc[d][4 * qd + 3] * inv);
+        gstore64(orow + 32 * d + 8 * qd + 4 * g, v2);
+      }
+    }
+    if (p.lse && g == 0) {
+      const float L = l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : INFINITY;
+      const int64_t li = p.cu_q ? (int64_t)h * p.total_q + q_start + my_row
+                                : ((int64_t)b * p.Hq + h) * Sq + my_row;
+      p.lse[li] = L;
+    }
+  }
+}
+
+template <int D, int DT>
+static void launch_fwd_dt(const FwdParams& prm, bool softcap, bool alibi, int nwg, hipStream_t st) {
+  dim3 grid(nwg), block(256);
+  if (softcap) {
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, true, true>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, true, false>), grid, block, 0, st, prm);
+  } else {
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, false, true>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, false, false>), grid, block, 0, st, prm);
+  }
+}
+
+static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap, int causal,
+                   int max_sq, int nbatch, hipStream_t st) {
+  prm.scale_log2 = scale * kLog2e;
+  prm.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
+  prm.cap_log2 = softcap * kLog2e;
+  if (causal) prm.wr = 0;
+  prm.n_qtiles = (max_sq + 127) / 128;
+  prm.n_heads = prm.Hq;
+  prm.n_batch = nbatch;
+  prm.reverse = causal ? 1 : 0;
+  const long long nwg = (long long)prm.n_qtiles * prm.n_heads * prm.n_batch;
+  if (nwg <= 0) return FA_OK;
+  if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  const bool sc = softcap > 0.0f, al = prm.alibi != nullptr;
+  prof_before(FA_KERNEL_FWD, st);
+  if (D == 128) {
+    if (dtype == FA_DTYPE_BF16) launch_fwd_dt<128, DT_BF16>(prm, sc, al, (int)nwg, st);
+    else launch_fwd_dt<128, DT_F16>(prm, sc, al, (int)nwg, st);
+  } else {
+    if (dtype == FA_DTYPE_BF16) launch_fwd_dt<64, DT_BF16>(prm, sc, al, (int)nwg, st);
+    else launch_fwd_dt<64, DT_F16>(prm, sc, al, (int)nwg, st);
+  }
+  prof_after(FA_KERNEL_FWD, st);
+  return launch_status();
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, void* stream) {
+  int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
+  if (st) return st;
+  if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
+  FwdParams prm{};
+  prm.q = (const uint16_t*)q;
+  prm.k = (const uint16_t*)k;
+  prm.v = (const uint16_t*)v;
+  prm.o = (uint16_t*)out;
+  prm.lse = lse;
+  prm.Sq = Sq;
+  prm.Sk = Sk;
+  prm.Hq = Hq;
+  prm.g = Hq / Hkv;
+  prm.q_rstride = Hq * D;
+  prm.k_rstride = Hkv * D;
+  prm.alibi = alibi_slopes;
+  prm.wl = window_left;
+  prm.wr = window_right;
+  return run_fwd(prm, D, dtype, scale, softcap, causal, Sq, B, (hipStream_t)stream);
+}
+
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                             int Hq, int Hkv, int D, int dtype,
+                             float scale, int causal, int window_left, int window_right, float softcap,
+                             const float* alibi_slopes, void* stream) {
+  int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
+  if (st) return st;
+  if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  FwdParams prm{};
+  prm.q = (const uint16_t*)q;
+  prm.k = (const uint16_t*)k;
+  prm.v = (const uint16_t*)v;
+  prm.o = (uint16_t*)out;
+  prm.lse = lse;
+  prm.cu_q = cu_seqlens_q;
+  prm.cu_k = cu_seqlens_k;
+  prm.Hq = Hq;
+  prm.g = Hq / Hkv;
+  prm.total_q = total_q;
+  prm.q_rstride = Hq * D;
+  prm.k_rstride = Hkv * D;
+  prm.alibi = alibi_slopes;
+  prm.wl = window_left;
+  prm.wr = window_right;
+  return run_fwd(prm, D, dtype, scale, softcap, causal, max_seqlen_q, nseq, (hipStream_t)stream);
+}

@@ -140,7 +140,7 @@ def attention_fwd(q, k, v, scale, causal=False, window=(-1, -1), softcap=0.0,
 
 
 def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, heads=None, k_rows=None, check_delta=True):
+                  alibi_slopes=None, heads=None, k_rows=None, q_rows=None, check_delta=True):
     """Analytic backward of standard attention in float64.
 
     The pages' method recomputes the attention matrix in the backward pass
@@ -161,7 +161,9 @@ def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0
     from them; ``k_rows`` restricts dk/dv to a subset of key rows (dq is then
     not computed).  With ``k_rows`` the row term delta_i is taken as
     dO_i . O_i, the same quantity (sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j),
-    so that full rows of dP are not needed.
+    so that full rows of dP are not needed.  ``q_rows`` restricts the work to
+    dq of those query rows (dk/dv are then not computed); each dq row needs
+    only its own row of P and dP.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, Sq, Hq, D = q.shape
@@ -177,12 +179,19 @@ def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0
         for h in heads:
             kh, vh, qh, doh = k[b, :, h // g, :], v[b, :, h // g, :], q[b, :, h, :], do[b, :, h, :]
             slope = None if slopes is None else slopes[h]
-            dq_h = np.zeros((Sq, D))
-            for c0 in range(0, Sq, ROW_CHUNK):
-                rows = np.arange(c0, min(Sq, c0 + ROW_CHUNK))
+            dq_h = np.full((Sq, D), np.nan) if q_rows is not None else np.zeros((Sq, D))
+            row_list = np.arange(Sq) if q_rows is None else np.asarray(q_rows, dtype=np.int64)
+            for c0 in range(0, len(row_list), ROW_CHUNK):
+                rows = row_list[c0:c0 + ROW_CHUNK]
                 z, t, ok = _row_block(qh, kh, rows, Sq, Sk, scale, causal, window, softcap, slope)
                 P, _ = _softmax_rows(z, ok)
-                if k_rows is None:
+                if q_rows is not None:
+                    dP = doh[rows] @ vh.T
+                    delta = (P * dP).sum(axis=1)
+                    dZ = P * (dP - delta[:, None])
+                    dS = dZ * (1.0 - t * t) if t is not None else dZ
+                    dq_h[rows] = scale * (dS @ kh)
+                elif k_rows is None:
                     dP = doh[rows] @ vh.T
                     delta = (P * dP).sum(axis=1)
                     if check_delta:
@@ -204,4 +213,7 @@ def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0
                     dv[b, cols, h // g, :] += Pc.T @ doh[rows]
             if k_rows is None:
                 dq[b, :, h, :] = dq_h
+    if q_rows is not None:
+        dk[:] = np.nan
+        dv[:] = np.nan
     return dq, dk, dv

@@ -62,15 +62,19 @@ def rotary_apply(x, cos_row, sin_row, rotary_dim):
 
 
 def gather_logical_cache(cache, b, L, block_table=None, page_size=None):
-    """Rows 0..L-1 of sequence b's logical cache, shape (L, Hkv, D) float64."""
-    cache = _f64(cache)
+    """Rows 0..L-1 of sequence b's logical cache, shape (L, Hkv, D) float64.
+    Rows are gathered first and converted afterwards, so only live rows are
+    ever widened to float64."""
     if block_table is None:
-        return cache[b, :L]
+        return _f64(cache[b, :L])
     bt = np.asarray(block_table.cpu().numpy() if hasattr(block_table, "cpu") else block_table)
     j = np.arange(L)
     pages = bt[b, j // page_size]
     assert (pages >= 0).all(), "block_table entry missing for a live position"
-    return cache[pages, j % page_size]
+    if hasattr(cache, "detach"):
+        import torch
+        return _f64(cache[torch.from_numpy(pages).long(), torch.from_numpy(j % page_size).long()])
+    return _f64(np.asarray(cache)[pages, j % page_size])
 
 
 def kvcache_fwd(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table=None,

@@ -1,0 +1,112 @@
+"""GPU parity of the paged KV-cache decode (split + combine) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_qk_amd as fa
+from oracle import kvcache_fwd
+from workloads import decode_case, cfg5
+from _helpers import DEV, assert_out, assert_lse, say, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, num_splits, append=True, block_table="given"):
+    q = c.q.to(DEV)
+    kc, vc = c.k_cache.to(DEV), c.v_cache.to(DEV)
+    bt = c.block_table.to(DEV) if (c.block_table is not None and block_table == "given") else None
+    rot = (c.rotary_cos.to(DEV), c.rotary_sin.to(DEV)) if c.rotary_cos is not None else (None, None)
+    out, lse = fa.fa_fwd_kvcache(q, kc, vc, c.cache_seqlens.to(DEV),
+                                 c.k_new.to(DEV) if append else None,
+                                 c.v_new.to(DEV) if append else None,
+                                 bt, rot[0], rot[1], c.rotary_dim if rot[0] is not None else None,
+                                 num_splits=num_splits, scale=c.scale)
+    torch.cuda.synchronize()
+    return out, lse, kc, vc
+
+
+def _oracle(c, append=True):
+    return kvcache_fwd(c.q, c.k_new if append else None, c.v_new if append else None, c.k_cache,
+                       c.v_cache, c.cache_seqlens, c.block_table, c.page_size, c.rotary_cos,
+                       c.rotary_sin, c.rotary_dim, c.scale, cache_dtype="bf16" if c.q.dtype == torch.bfloat16 else "fp16")
+
+
+def _check_cache(c, ref, kc, vc, paged=True):
+    """Appended slots hold the oracle's k_app (within 1 ulp when rotated) and
+    v_new exactly; every other cache byte is unchanged."""
+    k_after, v_after = kc.cpu(), vc.cpu()
+    k_before, v_before = c.k_cache.clone(), c.v_cache.clone()
+    for (b, t, phys) in ref["slots"]:
+        ka = k_after[phys[0], phys[1]].double().numpy()
+        ref_k = ref["k_app"][b, t]
+        if c.rotary_cos is None or c.rotary_dim == 0:
+            np.testing.assert_array_equal(ka, ref_k)
+        else:
+            ulp = np.abs(ref_k) * 2.0 ** -7 + 1e-30
+            assert (np.abs(ka - ref_k) <= ulp).all(), "appended key differs by more than 1 ulp"
+        np.testing.assert_array_equal(v_after[phys[0], phys[1]].double().numpy(), ref["v_app"][b, t])
+        k_before[phys[0], phys[1]] = k_after[phys[0], phys[1]]
+        v_before[phys[0], phys[1]] = v_after[phys[0], phys[1]]
+    assert torch.equal(k_before, k_after), "cache bytes outside the appended slots changed"
+    assert torch.equal(v_before, v_after), "cache bytes outside the appended slots changed"
+
+
+SMALL = [
+    # B, Hq, Hkv, D, page, seqlens, dtype, rotary_dim, paged
+    (3, 8, 2, 128, 64, [300, 77, 64], "bf16", 128, True),
+    (2, 4, 4, 64, 32, [31, 200], "fp16", 32, True),
+    (2, 32, 1, 128, 256, [1000, 1], "bf16", 0, True),
+    (4, 16, 4, 128, 128, [0, 5, 127, 128], "bf16", 64, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"d{i}" for i in range(len(SMALL))])
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+def test_small_decode(case, num_splits):
+    B, Hq, Hkv, D, page, lens, dt, rd, paged = case
+    c = decode_case(B=B, Hq=Hq, Hkv=Hkv, D=D, page=page, seqlens=lens, seed=51, dtype=dt,
+                    rotary_dim=rd, paged=paged)
+    say("decode small", case, num_splits)
+    out, lse, kc, vc = _run(c, num_splits)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc, paged)
+
+
+def test_decode_without_append():
+    c = decode_case(B=2, Hq=8, Hkv=2, D=128, page=64, seqlens=[150, 64], seed=52)
+    say("decode no append")
+    out, lse, kc, vc = _run(c, 2, append=False)
+    ref = _oracle(c, append=False)
+    assert_out(out, ref["out"], torch.bfloat16)
+    assert_lse(lse, ref["lse"])
+    assert torch.equal(kc.cpu(), c.k_cache) and torch.equal(vc.cpu(), c.v_cache)
+
+
+def test_block_table_permutation_bitwise():
+    c = decode_case(B=2, Hq=8, Hkv=2, D=128, page=64, seqlens=[500, 260], seed=53)
+    say("decode permuted pages")
+    o1, l1, _, _ = _run(c, 4)
+    n = c.k_cache.shape[0]
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(n))
+    inv = torch.argsort(perm)
+    c.k_cache = c.k_cache[perm].contiguous()
+    c.v_cache = c.v_cache[perm].contiguous()
+    live = c.block_table >= 0
+    bt = c.block_table.clone()
+    bt[live] = inv[c.block_table[live].long()].to(torch.int32)
+    c.block_table = bt
+    o2, l2, _, _ = _run(c, 4)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4, 16])
+def test_cfg5_full(num_splits):
+    c = cfg5()
+    say("decode", c.name, "splits", num_splits)
+    out, lse, kc, vc = _run(c, num_splits)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], torch.bfloat16)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)

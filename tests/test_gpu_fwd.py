@@ -1,0 +1,128 @@
+"""GPU parity of fa_fwd against the float64 oracle (runs on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_qk_amd as fa
+from oracle import attention_fwd
+from workloads import dense_case, cfg1, cfg2, cfg3, CFG2_SEQLENS
+from _helpers import DEV, assert_out, assert_lse, say, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c):
+    q, k, v = (t.to(DEV) for t in (c.q, c.k, c.v))
+    al = None if c.alibi_slopes is None else c.alibi_slopes.to(DEV)
+    out, lse = fa.fa_fwd(q, k, v, scale=c.scale, causal=c.causal, window=c.window, softcap=c.softcap,
+                         alibi_slopes=al)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_cfg1_full():
+    c = cfg1()
+    say("fwd", c.name)
+    out, lse = _run(c)
+    ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, causal=True)
+    assert_out(out, ro, torch.float16)
+    assert_lse(lse, rl)
+
+
+SMALL = [
+    # B, Sq, Sk, Hq, Hkv, D, dtype, causal, window, softcap, alibi
+    (2, 200, 200, 4, 4, 128, "bf16", False, (-1, -1), 0.0, False),
+    (1, 333, 333, 4, 2, 128, "bf16", True, (-1, -1), 0.0, False),
+    (2, 130, 257, 8, 2, 64, "fp16", True, (-1, -1), 0.0, False),
+    (1, 300, 100, 2, 1, 128, "bf16", True, (-1, -1), 0.0, False),
+    (1, 257, 257, 4, 1, 128, "bf16", True, (64, 0), 30.0, True),
+    (1, 190, 190, 2, 2, 64, "bf16", False, (17, 33), 0.0, False),
+    (1, 1, 1, 1, 1, 128, "bf16", False, (-1, -1), 0.0, False),
+    (3, 1, 77, 4, 4, 128, "fp16", True, (-1, -1), 0.0, False),
+    (2, 129, 129, 3, 3, 64, "fp16", False, (-1, -1), 5.0, False),
+    (1, 400, 380, 8, 8, 128, "fp16", False, (100, 7), 0.0, True),
+    (1, 64, 1000, 2, 2, 128, "bf16", True, (200, 0), 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{i}" for i in range(len(SMALL))])
+def test_small_cases(case):
+    B, Sq, Sk, Hq, Hkv, D, dt, causal, window, softcap, alibi = case
+    c = dense_case(B, Sq, Sk, Hq, Hkv, D, dt, seed=100 + Sq, causal=causal, window=window,
+                   softcap=softcap, alibi=alibi, with_dout=False)
+    say("fwd small", case)
+    out, lse = _run(c)
+    ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, causal, window, softcap, c.alibi_slopes)
+    assert_out(out, ro, c.q.dtype)
+    assert_lse(lse, rl)
+    # rows without a visible key: O = 0, LSE = +inf
+    empty = np.isinf(rl)
+    if empty.any():
+        o = np64(out).transpose(0, 2, 1, 3)
+        assert (o[empty] == 0).all() and np.isposinf(np64(lse)[empty]).all()
+
+
+def _sample_rows(S, n=6):
+    return sorted(set([0, 1, S // 3, S // 2, S - 2, S - 1][:n]))
+
+
+@pytest.mark.parametrize("S", CFG2_SEQLENS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hd", [(16, 128), (32, 64)])
+def test_cfg2_full_size_sampled(S, causal, hd):
+    H, D = hd
+    c = cfg2(S, H, D, causal)
+    say("fwd", c.name)
+    out, lse = _run(c)
+    rows = _sample_rows(S)
+    heads = [0, H - 1]
+    ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, causal, heads=heads, q_rows=rows)
+    m_o = np.zeros(ro.shape, bool)
+    m_l = np.zeros(rl.shape, bool)
+    for h in heads:
+        m_o[:, rows, h, :] = True
+        m_l[:, h, rows] = True
+    assert_out(out, ro, torch.bfloat16, mask=m_o)
+    assert_lse(lse, rl, mask=m_l)
+    assert torch.isfinite(out).all()
+
+
+def test_cfg3_full_size_sampled():
+    c = cfg3()
+    say("fwd", c.name)
+    out, lse = _run(c)
+    rows = [0, 1, 100, 4095, 4096, 4097, 6000, 8190, 8191]
+    heads = [0, 13, 31]
+    ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, True, c.window, c.softcap, c.alibi_slopes,
+                           heads=heads, q_rows=rows)
+    m_o = np.zeros(ro.shape, bool)
+    m_l = np.zeros(rl.shape, bool)
+    for h in heads:
+        m_o[:, rows, h, :] = True
+        m_l[:, h, rows] = True
+    assert_out(out, ro, torch.bfloat16, mask=m_o)
+    assert_lse(lse, rl, mask=m_l)
+
+
+def test_bitwise_repeatable():
+    c = dense_case(2, 300, 300, 4, 2, 128, "bf16", seed=5, causal=True)
+    say("fwd repeat")
+    a, la = _run(c)
+    b, lb = _run(c)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_guard_bands_untouched():
+    # outputs live inside larger buffers: nothing outside the view is written
+    c = dense_case(1, 150, 150, 2, 2, 128, "bf16", seed=6, causal=True, with_dout=False)
+    q, k, v = (t.to(DEV) for t in (c.q, c.k, c.v))
+    n = q.numel()
+    big = torch.full((n + 4096,), 7.0, device=DEV, dtype=q.dtype)
+    out = big[2048:2048 + n].view(q.shape)
+    lbig = torch.full((2 * 150 + 2048,), 7.0, device=DEV)
+    lse = lbig[1024:1024 + 300].view(1, 2, 150)
+    say("fwd guard bands")
+    fa.fa_fwd(q, k, v, out=out, lse=lse, scale=c.scale, causal=True)
+    torch.cuda.synchronize()
+    assert (big[:2048] == 7).all() and (big[2048 + n:] == 7).all()
+    assert (lbig[:1024] == 7).all() and (lbig[1324:] == 7).all()

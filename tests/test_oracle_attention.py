@@ -370,3 +370,6 @@ def test_sampled_modes_match_full():
     _, dks, dvs = attention_bwd(c.q, c.k, c.v, c.dout, *args, k_rows=kr)
     np.testing.assert_allclose(dks[:, kr], dk[:, kr], atol=1e-12)
     np.testing.assert_allclose(dvs[:, kr], dv[:, kr], atol=1e-12)
+    qr = [1, 20, 39]
+    dqs, _, _ = attention_bwd(c.q, c.k, c.v, c.dout, *args, heads=[0, 2], q_rows=qr)
+    np.testing.assert_allclose(dqs[:, qr][:, :, [0, 2]], dq[:, qr][:, :, [0, 2]], atol=1e-12)
