@@ -96,8 +96,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
            const float* alibi_slopes, int deterministic,
            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fa_bwd needs (host-only, pure): a float32 row term
- * (B, Hq, Sq) plus alignment padding. */
+/* Bytes of workspace fa_bwd needs (host-only, pure): two float32 row arrays
+ * (B, Hq, Sq) -- the row term sum_d dO*O and the LSE in log2 units -- each
+ * padded to 256 bytes. */
 size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int deterministic);
 
 /*
@@ -126,7 +127,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
                   const float* alibi_slopes, int deterministic,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace for fa_bwd_varlen: float32 (Hq, total_q) row term plus padding. */
+/* Workspace for fa_bwd_varlen: two float32 (Hq, total_q) row arrays, each
+ * padded to 256 bytes. */
 size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic);
 
 /*

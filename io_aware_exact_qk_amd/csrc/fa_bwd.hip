@@ -11,15 +11,18 @@
 //
 // Three kernels, none with atomics, so every result is bitwise reproducible
 // (the pages' deterministic=True option is therefore always satisfied):
-//   1. row term  delta_i = sum_d dO_id O_id  (float32);
+//   1. row terms  delta_i = sum_d dO_id O_id  and  LSE_i log2(e)  (float32);
 //   2. dK/dV: one work-group per 128 keys of one K/V head; each wave keeps 32
 //      keys' K and V rows in VGPRs and walks every query head of its group and
-//      every query tile of 32 rows in a fixed order, with Q and dO tiles
-//      staged in LDS.  S = Q K^T puts one key per lane, so dV^T += dO^T P and
-//      dK^T += Q^T dS take P / dS straight from the accumulators;
+//      every query tile of 64 rows in a fixed order, with Q and dO tiles
+//      copied into LDS by DMA.  S = Q K^T puts one key per lane, so
+//      dV^T += dO^T P and dK^T += Q^T dS take P / dS straight from the
+//      accumulators;
 //   3. dQ: one work-group per 128 query rows of one query head (same layout
 //      as the forward); it recomputes S^T and dP^T per key tile and
 //      accumulates dQ^T += K^T dS^T.
+// Both recompute kernels fit in 256 VGPRs, so two waves share each SIMD and
+// one wave's exponentials overlap the other's matrix instructions.
 #include "fa_device.h"
 #include "fa_host.h"
 
@@ -32,7 +35,8 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float* dvec;  // workspace: row term, same layout as lse
+  float* dvec;  // workspace: row term delta, same layout as lse
+  float* lse2;  // workspace: lse * log2(e), same layout as lse
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -72,7 +76,9 @@ __device__ __forceinline__ int64_t row_index(const BwdParams& p, int b, int h, i
 }
 
 // ------------------------------------------------------------ row term ----
-// One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).
+// One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).  Writes
+// delta = sum_d dO O and the forward's LSE in log2 units, the two per-row
+// values the recompute kernels need.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int NCH = D / 8;
@@ -102,6 +108,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
       idx = ((int64_t)b * p.Hq + h) * p.Sq + i;
     }
     p.dvec[idx] = acc;
+    p.lse2[idx] = p.lse[idx] * kLog2e;
   }
 }
 
@@ -123,13 +130,15 @@ __device__ __forceinline__ float logit2(float s, int ip, int j, const BwdParams&
 }
 
 // --------------------------------------------------------------- dK / dV --
+// Work-group = 128 keys of one K/V head, 4 waves of 32 keys, two work-groups
+// per CU.  Query tiles of 64 rows (Q, dO, LSE, delta) are copied into LDS by
+// DMA, double buffered; the copy of tile n+1 runs under the matrix work of
+// tile n.
 template <int D, int DT, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BC = 128, BR = 32;
-  constexpr int NCH = D / 8, KC = D / 16, DB = D / 32;
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BC = 128, BR = 64;
+  constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BR * D * 2;
-  constexpr int RPP = 256 / NCH;
-  constexpr int PASSES = (BR + RPP - 1) / RPP;
   constexpr int STAGE = 2 * TILE + 2 * BR * 4;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -169,65 +178,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   int i_lo = 0, i_hi = Sq;
   if (p.wr >= 0) i_lo = max(0, k0 - p.wr - off);
   if (p.wl >= 0) i_hi = min(Sq, k1 + p.wl - off + 1);
-  if (i_lo < i_hi && Sq > 0) {
+  if (i_lo < i_hi) {
     const int t_lo = i_lo / BR, nt = (i_hi + BR - 1) / BR - t_lo;
     const int n_iter = nt * p.g;
-    const int lrow = tid / NCH, lch = tid % NCH;
-    u32x4 qpre[PASSES], dopre[PASSES];
-    float lpre = 0.0f, dpre = 0.0f;
-    auto load = [&](int n) {
+    auto issue = [&](int n, int buf) {
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
-      const int64_t hoff = (int64_t)hq * D;
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int row = lrow + it * RPP;
-        const int i = i0 + row;
-        if (row < BR && i < Sq) {
-          const int64_t a = (int64_t)(sb.q_start + i) * p.q_rstride + hoff + lch * 8;
-          qpre[it] = gload128(p.q + a);
-          dopre[it] = gload128(p.dout + a);
-        } else {
-          qpre[it] = u32x4{0, 0, 0, 0};
-          dopre[it] = u32x4{0, 0, 0, 0};
-        }
-      }
-      if (tid < BR) {
-        const int i = i0 + tid;
-        if (i < Sq) {
-          const int64_t ri = row_index(p, b, hq, sb.q_start, Sq, i);
-          lpre = p.lse[ri] * kLog2e;
-          dpre = p.dvec[ri];
-        } else {
-          lpre = INFINITY;
-          dpre = 0.0f;
-        }
-      }
-    };
-    auto store = [&](int buf) {
       char* st = smem + buf * STAGE;
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int row = lrow + it * RPP;
-        if (row < BR) {
-          const uint32_t o = tile_off<D>(row, lch);
-          lds_write128(st, o, qpre[it]);
-          lds_write128(st + TILE, o, dopre[it]);
-        }
-      }
-      if (tid < BR) {
-        reinterpret_cast<float*>(st + 2 * TILE)[tid] = lpre;
-        reinterpret_cast<float*>(st + 2 * TILE + BR * 4)[tid] = dpre;
+      const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * D;
+      dma_tile<D, BR, 4>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, 4>(st + TILE, p.dout + hoff, p.q_rstride, i0, Sq, w, lane);
+      if (w < 2) {
+        const float* src = (w == 0) ? p.lse2 : p.dvec;
+        const int i = min(i0 + lane, Sq - 1);
+        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + 2 * TILE + w * BR * 4);
       }
     };
 
-    load(0);
-    store(0);
+    issue(0, 0);
+    dma_wait();
     __syncthreads();
     for (int n = 0; n < n_iter; ++n) {
       const int buf = n & 1;
-      const bool more = n + 1 < n_iter;
-      if (more) load(n + 1);
+      if (n + 1 < n_iter) issue(n + 1, buf ^ 1);
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
       const char* st = smem + buf * STAGE;
@@ -235,30 +208,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const char* dot = st + TILE;
       const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
       const float* dvs = lse2 + BR;
-      const int i1 = min(i0 + BR - 1, Sq - 1);
-      const int cls = classify(i0 + off, i1 + off, kw0, kw0 + 31, Sk, mask);
-      if (cls != 0) {
-        const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
+      const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
+#pragma unroll
+      for (int rb = 0; rb < BR / 32; ++rb) {
+        const int r0 = i0 + 32 * rb;
+        if (r0 >= Sq) break;
+        int cls = classify(r0 + off, min(r0 + 31, Sq - 1) + off, kw0, kw0 + 31, Sk, mask);
+        if (cls == 0) continue;
+        if (r0 + 31 >= Sq) cls = 1;  // rows past the end hold a copy of the last row
         // S = Q K^T and dP = dO V^T: rows = 32 queries, columns = this wave's keys
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          s = mfma32<DT>(lds_read_nat<D>(qt, r, 2 * c + g), kreg[c], s);
-          dp = mfma32<DT>(lds_read_nat<D>(dot, r, 2 * c + g), vreg[c], dp);
+          s = mfma32<DT>(lds_read_nat<D>(qt, 32 * rb + r, 2 * c + g), kreg[c], s);
+          dp = mfma32<DT>(lds_read_nat<D>(dot, 32 * rb + r, 2 * c + g), vreg[c], dp);
         }
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * qd + 4 * g);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvs + 8 * qd + 4 * g);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 32 * rb + 8 * qd + 4 * g);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvs + 32 * rb + 8 * qd + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int ii = 4 * qd + e;
-            const int row = i0 + frag_row(ii, g);
+            const int row = r0 + frag_row(ii, g);
             const int ip = row + off;
             float t;
             const float x = logit2<SOFTCAP, ALIBI>(s[ii], ip, my_key, p, slope_log2, t);
             float pv = fast_exp2(x - l4[e]);
-            if (cls == 1 && !(key_ok && visible(ip, my_key, Sk, mask))) pv = 0.0f;
+            if (cls == 1 && !(row < Sq && key_ok && visible(ip, my_key, Sk, mask))) pv = 0.0f;
             float ds = pv * (dp[ii] - d4[e]);
             if constexpr (SOFTCAP) ds *= (1.0f - t * t);
             s[ii] = pv;
@@ -272,12 +249,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           const u32x4 sb2 = pack_frag_half<DT>(dp, mk);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            dvacc[d] = mfma32<DT>(lds_read_At<D>(dot, 16 * mk, 32 * d, lane), pb, dvacc[d]);
-            dkacc[d] = mfma32<DT>(lds_read_At<D>(qt, 16 * mk, 32 * d, lane), sb2, dkacc[d]);
+            dvacc[d] = mfma32<DT>(lds_read_At<D>(dot, 32 * rb + 16 * mk, 32 * d, lane), pb, dvacc[d]);
+            dkacc[d] = mfma32<DT>(lds_read_At<D>(qt, 32 * rb + 16 * mk, 32 * d, lane), sb2, dkacc[d]);
           }
         }
       }
-      if (more) store(buf ^ 1);
+      dma_wait();
       __syncthreads();
     }
   }
@@ -302,13 +279,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ dQ ----
+// Work-group = 128 query rows of one query head (4 waves of 32 rows), two
+// work-groups per CU; K/V tiles of 64 keys are copied into LDS by DMA,
+// double buffered.
 template <int D, int DT, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 128, BC = 64;
-  constexpr int NCH = D / 8, KC = D / 16, DB = D / 32;
+  constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BC * D * 2;
-  constexpr int RPP = 256 / NCH;
-  constexpr int PASSES = BC / RPP;
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -339,10 +317,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     qreg[c] = row_ok ? gload128(p.q + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
     doreg[c] = row_ok ? gload128(p.dout + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
-  float lse2 = INFINITY, dv_row = 0.0f;
+  float lse2 = INFINITY, dv_row = 0.0f;  // rows past the end: P = 0
   if (row_ok) {
     const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
-    lse2 = p.lse[ri] * kLog2e;
+    lse2 = p.lse2[ri];
     dv_row = p.dvec[ri];
   }
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
@@ -360,41 +338,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    const int lrow = tid / NCH, lch = tid % NCH;
-    u32x4 kpre[PASSES], vpre[PASSES];
-    auto load_tile = [&](int t) {
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int j = t * BC + lrow + it * RPP;
-        if (j < Sk) {
-          kpre[it] = gload128(kbase + (int64_t)j * p.k_rstride + lch * 8);
-          vpre[it] = gload128(vbase + (int64_t)j * p.k_rstride + lch * 8);
-        } else {
-          kpre[it] = u32x4{0, 0, 0, 0};
-          vpre[it] = u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    auto store_tile = [&](int buf) {
+    auto issue = [&](int t, int buf) {
       char* kt = smem + buf * 2 * TILE;
-      char* vt = kt + TILE;
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const uint32_t o = tile_off<D>(lrow + it * RPP, lch);
-        lds_write128(kt, o, kpre[it]);
-        lds_write128(vt, o, vpre[it]);
-      }
+      dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
-    load_tile(t_lo);
-    store_tile(0);
+    issue(t_lo, 0);
+    dma_wait();
     __syncthreads();
     for (int t = t_lo; t < t_hi; ++t) {
       const int buf = (t - t_lo) & 1;
-      const bool more = t + 1 < t_hi;
-      if (more) load_tile(t + 1);
+      if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
       const char* kt = smem + buf * 2 * TILE;
       const char* vt = kt + TILE;
       const int j0 = t * BC;
+      // keys past the end hold a copy of the last key: classify marks such tiles partial
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
       if (cls != 0) {
         f32x16 s[2], dp[2];
@@ -432,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           }
         }
       }
-      if (more) store_tile(buf ^ 1);
+      dma_wait();
       __syncthreads();
     }
   }
@@ -556,14 +514,14 @@ extern "C" size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, 
   (void)D;
   (void)deterministic;
   if (B < 1 || Sq < 1 || Hq < 1) return 0;
-  return align_up((size_t)B * Hq * Sq * sizeof(float), 256);
+  return 2 * align_up((size_t)B * Hq * Sq * sizeof(float), 256);
 }
 
 extern "C" size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic) {
   (void)D;
   (void)deterministic;
   if (total_q < 0 || Hq < 1) return 0;
-  return align_up((size_t)total_q * Hq * sizeof(float), 256);
+  return 2 * align_up((size_t)total_q * Hq * sizeof(float), 256);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -582,6 +540,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
               alibi_slopes);
   p.dvec = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + need / 2);
   p.Sq = Sq;
   p.Sk = Sk;
   return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, B * Sq, causal, (hipStream_t)stream);
@@ -607,6 +566,7 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
   fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
               alibi_slopes);
   p.dvec = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + need / 2);
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;

@@ -143,6 +143,48 @@ __device__ __forceinline__ u32x4 lds_read_nat(const char* smem, int row, int chu
   return lds_read128(smem, tile_off<D>(row, chunk));
 }
 
+// ----------------------------------------------------- global -> LDS DMA --
+// global_load_lds_dwordx4: every lane fetches 16 bytes from its own global
+// address and the hardware writes lane l's bytes to LDS at base + 16 * l, so
+// one instruction fills one contiguous 1 KB block without passing through
+// VGPRs.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, char* lds_block) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
+}
+
+// 4-byte variant: lane l's dword lands at base + 4 * l.
+__device__ __forceinline__ void dma4(const void* src, char* lds_block) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 4, 0, 0);
+}
+
+// Wait until every DMA (and global load) this wave issued has landed.
+// Encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Rows [row0, row0 + ROWS) of a row-major 16-bit matrix with D columns and a
+// row stride of `rstride` elements, copied into an LDS tile laid out as
+// tile_off<D>.  The 1 KB blocks of the tile are dealt to the NWAVES waves;
+// lane l of a block writes physical chunk l % (D/8) of its row, so it loads
+// the logical chunk that the swizzle maps there.  Rows at or past `nrows`
+// (>= 1) re-read row nrows - 1 (valid memory); callers mask those rows.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64_t rstride, int row0,
+                                         int nrows, int w, int lane) {
+  constexpr int NCH = D / 8, RPB = 64 / NCH, NBLK = ROWS / RPB;
+  static_assert(NBLK % NWAVES == 0, "tile blocks must divide among the waves");
+  const int rin = lane / NCH, pch = lane % NCH;
+#pragma unroll
+  for (int i = 0; i < NBLK / NWAVES; ++i) {
+    const int blk = i * NWAVES + w;
+    const int row = blk * RPB + rin;
+    const int lch = pch ^ (int)swz(row);
+    const int grow = min(row0 + row, nrows - 1);
+    dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+  }
+}
+
 // ------------------------------------------------------------ wave utils --
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
