@@ -44,7 +44,7 @@ struct BwdParams {
   const int* cu_k;
   int Sq, Sk, Hq, g, total_q;
   int q_rstride, k_rstride;
-  float scale, scale_log2, scale_over_cap, cap_log2;
+  float scale, scale_log2, scale_over_cap, cap_log2, inv_cap_log2;
   const float* alibi;
   int wl, wr;
   int n_tiles, n_heads, n_batch, reverse;
@@ -113,20 +113,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // --------------------------------------------------- logit transform ------
-// Log2-domain logit x of raw dot product s for query position ip, key j;
-// also returns t = tanh(s * scale / c) for the softcap derivative.
+// Log2-domain logit of raw dot product s for query position ip, key j, when
+// softcap or ALiBi is on (otherwise the scale is folded into the exponent).
 template <bool SOFTCAP, bool ALIBI>
-__device__ __forceinline__ float logit2(float s, int ip, int j, const BwdParams& p, float slope_log2, float& t) {
-  float x;
-  if constexpr (SOFTCAP) {
-    t = tanh_exp(s * p.scale_over_cap);
-    x = p.cap_log2 * t;
-  } else {
-    t = 0.0f;
-    x = s * p.scale_log2;
-  }
+__device__ __forceinline__ float logit2(float s, int ip, int j, const BwdParams& p, float slope_log2) {
+  float x = SOFTCAP ? p.cap_log2 * tanh_exp(s * p.scale_over_cap) : s * p.scale_log2;
   if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
   return x;
+}
+
+// dS = dZ * (1 - tanh^2(s/c)) with softcap c; tanh is recovered from the
+// log2 logit x = c log2(e) tanh(s/c) - ALiBi term.  Masked entries (p = 0,
+// x = -inf) stay 0.
+template <bool ALIBI>
+__device__ __forceinline__ float softcap_grad(float ds, float pv, float x, int ip, int j, const BwdParams& p,
+                                              float slope_log2) {
+  float xt = x;
+  if constexpr (ALIBI) xt += slope_log2 * (float)abs(ip - j);
+  const float t = xt * p.inv_cap_log2;
+  return pv > 0.0f ? ds * fmaf(-t, t, 1.0f) : 0.0f;
 }
 
 // --------------------------------------------------------------- dK / dV --
@@ -144,6 +149,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
+  const uint32_t nb = nat_base<D>(lane);
+  const uint32_t tb = tr_base<D>(lane);
   const int nwg = p.n_tiles * p.n_heads * p.n_batch;
   const int id = xcd_remap((int)blockIdx.x, nwg);
   const int tk = id % p.n_tiles;
@@ -209,6 +216,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
       const float* dvs = lse2 + BR;
       const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
+      const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
 #pragma unroll
       for (int rb = 0; rb < BR / 32; ++rb) {
         const int r0 = i0 + 32 * rb;
@@ -220,8 +228,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          s = mfma32<DT>(lds_read_nat<D>(qt, 32 * rb + r, 2 * c + g), kreg[c], s);
-          dp = mfma32<DT>(lds_read_nat<D>(dot, 32 * rb + r, 2 * c + g), vreg[c], dp);
+          s = mfma32<DT>(lds_nat(lds_addr(qt) + nb + (32 * rb) * (D * 2), c), kreg[c], s);
+          dp = mfma32<DT>(lds_nat(lds_addr(dot) + nb + (32 * rb) * (D * 2), c), vreg[c], dp);
+        }
+        // logits, mask (rows past Sq hold a copy of the last row), P and dS
+        if constexpr (SOFTCAP || ALIBI) {
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int ip = r0 + frag_row(ii, g) + off;
+            s[ii] = logit2<SOFTCAP, ALIBI>(s[ii], ip, my_key, p, slope_log2);
+          }
+        }
+        if (cls == 1) {
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int row = r0 + frag_row(ii, g);
+            const bool ok = (row < Sq) & key_ok & visible(row + off, my_key, Sk, mask);
+            s[ii] = ok ? s[ii] : -INFINITY;
+          }
         }
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
@@ -230,14 +254,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int ii = 4 * qd + e;
-            const int row = r0 + frag_row(ii, g);
-            const int ip = row + off;
-            float t;
-            const float x = logit2<SOFTCAP, ALIBI>(s[ii], ip, my_key, p, slope_log2, t);
-            float pv = fast_exp2(x - l4[e]);
-            if (cls == 1 && !(row < Sq && key_ok && visible(ip, my_key, Sk, mask))) pv = 0.0f;
+            const float pv = fast_exp2(fmaf(s[ii], fs, -l4[e]));
             float ds = pv * (dp[ii] - d4[e]);
-            if constexpr (SOFTCAP) ds *= (1.0f - t * t);
+            if constexpr (SOFTCAP) {
+              ds = softcap_grad<ALIBI>(ds, pv, s[ii], r0 + frag_row(ii, g) + off, my_key, p, slope_log2);
+            }
             s[ii] = pv;
             dp[ii] = ds;
           }
@@ -249,8 +270,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
           const u32x4 sb2 = pack_frag_half<DT>(dp, mk);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            dvacc[d] = mfma32<DT>(lds_read_At<D>(dot, 32 * rb + 16 * mk, 32 * d, lane), pb, dvacc[d]);
-            dkacc[d] = mfma32<DT>(lds_read_At<D>(qt, 32 * rb + 16 * mk, 32 * d, lane), sb2, dkacc[d]);
+            dvacc[d] = mfma32<DT>(lds_At<D>(lds_addr(dot) + tb + (32 * rb + 16 * mk) * (D * 2), d), pb, dvacc[d]);
+            dkacc[d] = mfma32<DT>(lds_At<D>(lds_addr(qt) + tb + (32 * rb + 16 * mk) * (D * 2), d), sb2, dkacc[d]);
           }
         }
       }
@@ -291,6 +312,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
+  const uint32_t nb = nat_base<D>(lane);
+  const uint32_t tb = tr_base<D>(lane);
   const int nwg = p.n_tiles * p.n_heads * p.n_batch;
   const int id = xcd_remap((int)blockIdx.x, nwg);
   int tq = id % p.n_tiles;
@@ -324,6 +347,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     dv_row = p.dvec[ri];
   }
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
+  const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -362,21 +386,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
           dp[kb] = f32x16{};
 #pragma unroll
           for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_read_nat<D>(kt, kb * 32 + r, 2 * c + g), qreg[c], s[kb]);
-            dp[kb] = mfma32<DT>(lds_read_nat<D>(vt, kb * 32 + r, 2 * c + g), doreg[c], dp[kb]);
+            s[kb] = mfma32<DT>(lds_nat(lds_addr(kt) + nb + (kb * 32) * (D * 2), c), qreg[c], s[kb]);
+            dp[kb] = mfma32<DT>(lds_nat(lds_addr(vt) + nb + (kb * 32) * (D * 2), c), doreg[c], dp[kb]);
           }
+        }
+        // logits, mask (keys past Sk hold a copy of the last key), P and dS
+        if constexpr (SOFTCAP || ALIBI) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = j0 + 32 * kb + frag_row(i, g);
+              s[kb][i] = logit2<SOFTCAP, ALIBI>(s[kb][i], ip, j, p, slope_log2);
+            }
+        }
+        if (cls == 1) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = j0 + 32 * kb + frag_row(i, g);
+              s[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? s[kb][i] : -INFINITY;
+            }
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = j0 + 32 * kb + frag_row(i, g);
-            float t;
-            const float x = logit2<SOFTCAP, ALIBI>(s[kb][i], ip, j, p, slope_log2, t);
-            float pv = fast_exp2(x - lse2);
-            if (cls == 1 && !(row_ok && visible(ip, j, Sk, mask))) pv = 0.0f;
+            const float pv = fast_exp2(fmaf(s[kb][i], fs, -lse2));
             float ds = pv * (dp[kb][i] - dv_row);
-            if constexpr (SOFTCAP) ds *= (1.0f - t * t);
+            if constexpr (SOFTCAP) {
+              ds = softcap_grad<ALIBI>(ds, pv, s[kb][i], ip, j0 + 32 * kb + frag_row(i, g), p, slope_log2);
+            }
             dp[kb][i] = ds;
           }
         }
@@ -386,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
           const u32x4 db = pack_frag_half<DT>(dp[mk >> 1], mk & 1);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            dqacc[d] = mfma32<DT>(lds_read_At<D>(kt, 16 * mk, 32 * d, lane), db, dqacc[d]);
+            dqacc[d] = mfma32<DT>(lds_At<D>(lds_addr(kt) + tb + (16 * mk) * (D * 2), d), db, dqacc[d]);
           }
         }
       }
@@ -493,6 +534,7 @@ static void fill_common(BwdParams& p, const void* q, const void* k, const void* 
   p.scale_log2 = scale * kLog2e;
   p.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
   p.cap_log2 = softcap * kLog2e;
+  p.inv_cap_log2 = softcap > 0.0f ? 1.0f / (softcap * kLog2e) : 0.0f;
   p.alibi = alibi;
   p.wl = wl;
   p.wr = wr;

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, r = lane & 31;
+  const uint32_t tb = tr_base<D>(lane);
   const int s_id = blockIdx.x % p.num_splits;
   const int hkv = (blockIdx.x / p.num_splits) % p.Hkv;
   const int b = blockIdx.x / (p.num_splits * p.Hkv);
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
       for (int mk = 0; mk < 2; ++mk) {
         const u32x4 pb = pack_frag_half<DT>(s, mk);
 #pragma unroll
-        for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_read_At<D>(vt, 16 * mk, 32 * d, lane), pb, oacc[d]);
+        for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_At<D>(lds_addr(vt) + tb + (16 * mk) * (D * 2), d), pb, oacc[d]);
       }
     }
   }

@@ -90,16 +90,31 @@ __device__ __forceinline__ int frag_row(int i, int g) { return 8 * (i >> 2) + 4 
 
 // ------------------------------------------------------------- LDS tiles --
 // A tile is ROWS x D 16-bit elements stored row-major; its 16-byte chunks are
-// permuted within each row by an XOR so that
-//  * 8 consecutive rows read at the same logical chunk (ds_read_b128, A/B
-//    operands in natural order) touch 8 different bank groups, and
-//  * the 4 rows x 2 chunks fetched by one 16-lane group of a transposed read
-//    touch 8 different bank groups.
-__device__ __forceinline__ uint32_t swz(int row) { return (uint32_t)(((row & 3) << 1) | ((row >> 2) & 1)); }
+// permuted within each row by an XOR with swz<D>(row).  The LDS returns 256
+// bytes per clock: a ds_read_b128 is served 16 lanes at a time and a
+// ds_read_b64_tr_b16 32 lanes at a time, and two addresses in the same clock
+// conflict when they fall in the same 16-byte slot of a 256-byte line.  The
+// permutation is chosen so that
+//  * 16 consecutive rows read at one logical chunk (natural-order operands)
+//    land in 16 different slots, and
+//  * the 4 rows x 4 chunks of one half-wave transposed read (rows 4m..4m+3,
+//    chunks 4n..4n+3) land in 16 different slots.
+// D = 128 (16 chunks, one row per line): the low two row bits pick which
+// aligned group of 4 chunks, the next two permute inside it.  D = 64
+// (8 chunks, two rows per line, row parity picks the half line): row bit 1
+// picks the group of 4 chunks, row bits 2-3 permute inside it.
+template <int D>
+__device__ __forceinline__ uint32_t swz(int row) {
+  if constexpr (D == 128) {
+    return (uint32_t)(((row & 3) << 2) | ((row >> 2) & 3));
+  } else {
+    return (uint32_t)((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  }
+}
 
 template <int D>
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)row * (D * 2) + (((uint32_t)chunk ^ swz(row)) << 4);
+  return (uint32_t)row * (D * 2) + (((uint32_t)chunk ^ swz<D>(row)) << 4);
 }
 
 // Byte offset of element (row, col) where col is a multiple of 4.
@@ -143,6 +158,70 @@ __device__ __forceinline__ u32x4 lds_read_nat(const char* smem, int row, int chu
   return lds_read128(smem, tile_off<D>(row, chunk));
 }
 
+// Offsets in XOR form.  Because row * 2D has no bits inside the chunk field,
+//   tile_off(row, k) = row_base(row) ^ (k << 4),
+// and swz depends on row % 16 only, so for R0 a multiple of 16
+//   row_base(R0 + r) = R0 * 2D + row_base(r).
+// A kernel therefore keeps one per-lane base and forms each LDS address with
+// one XOR against a compile-time constant.
+template <int D>
+__device__ __forceinline__ uint32_t row_base(int row) {
+  return (uint32_t)row * (D * 2) + (swz<D>(row) << 4);
+}
+
+// 32-bit LDS byte address of a pointer into __shared__ memory, and reads at
+// such addresses.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+__device__ __forceinline__ u32x4 lds_ld128(uint32_t a) { return *(const lds_u32x4*)a; }
+__device__ __forceinline__ u32x2 lds_ld_tr(uint32_t a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a));
+}
+
+// Natural-order operand offset of a lane: row r = lane % 32 of a 32-row block,
+// chunk half g = lane / 32 folded in.
+template <int D>
+__device__ __forceinline__ uint32_t nat_base(int lane) {
+  return row_base<D>(lane & 31) ^ ((uint32_t)(lane >> 5) << 4);
+}
+
+// Step c (16 contraction elements: chunks 2c and 2c + 1) of a natural-order
+// operand.  `a` = LDS address of the operand's first row (256-byte aligned,
+// 16-row aligned within its tile) + the lane's nat_base.  The XOR is applied
+// after the per-iteration tile address is added, so no per-step address is
+// held in a register across the loop.
+__device__ __forceinline__ u32x4 lds_nat(uint32_t a, int c) { return lds_ld128(a ^ ((uint32_t)c << 5)); }
+
+// Transposed (acc-order) operand offset of a lane for lds_At: byte offset,
+// relative to a 16-row-aligned row0, of the 4-element piece it fetches from
+// row 4g'+(i/4) (g' = lane/32, i = lane%16), columns 16*((lane/16)%2) + 4*(i%4)
+// of a 32-column block.  The piece 8 rows below sits at (offset ^ 32) + 16D:
+// swz(rr + 8) = swz(rr) ^ 2 for both tile widths.
+template <int D>
+__device__ __forceinline__ uint32_t tr_base(int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int rr = 4 * (grp >> 1) + (i >> 2);
+  const int col = 16 * (grp & 1) + 4 * (i & 3);
+  return (row_base<D>(rr) ^ ((uint32_t)(col >> 3) << 4)) | ((uint32_t)(col & 7) << 1);
+}
+
+// A operand (32 x 16) whose 32 rows are tile columns 32d .. 32d+31 and whose
+// contraction runs over 16 tile rows.  `a` = LDS address of the first of those
+// rows (256-byte aligned, 16-row aligned within its tile) + the lane's tr_base.
+template <int D>
+__device__ __forceinline__ u32x4 lds_At(uint32_t a, int d) {
+  const uint32_t lo = a ^ ((uint32_t)d << 6);  // column block d = chunks 4d .. 4d+3
+  const u32x2 x = lds_ld_tr(lo);
+  const u32x2 y = lds_ld_tr((lo ^ 32u) + 8 * (D * 2));
+  u32x4 out = {x[0], x[1], y[0], y[1]};
+  return out;
+}
+
 // ----------------------------------------------------- global -> LDS DMA --
 // global_load_lds_dwordx4: every lane fetches 16 bytes from its own global
 // address and the hardware writes lane l's bytes to LDS at base + 16 * l, so
@@ -179,7 +258,7 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64
   for (int i = 0; i < NBLK / NWAVES; ++i) {
     const int blk = i * NWAVES + w;
     const int row = blk * RPB + rin;
-    const int lch = pch ^ (int)swz(row);
+    const int lch = pch ^ (int)swz<D>(row);
     const int grow = min(row0 + row, nrows - 1);
     dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
   }
@@ -213,8 +292,10 @@ struct MaskSpec {
   int wl, wr;  // -1 = unbounded
 };
 
+// Bitwise (not short-circuit) operators keep this a few VALU compares and no
+// branches when it is evaluated per element.
 __device__ __forceinline__ bool visible(int ip, int j, int Sk, MaskSpec m) {
-  return j < Sk && (m.wl < 0 || j >= ip - m.wl) && (m.wr < 0 || j <= ip + m.wr);
+  return (j < Sk) & ((m.wl < 0) | (j >= ip - m.wl)) & ((m.wr < 0) | (j <= ip + m.wr));
 }
 
 // Block-level classification for query positions [ip0, ip1] and keys [j0, j1].

@@ -9,8 +9,9 @@
 // Work decomposition (one work-group = 4 waves = 128 query rows of one head):
 //   * each wave owns 32 query rows; their Q fragment stays in VGPRs for the
 //     whole key loop (B operand of S^T = K Q^T);
-//   * K and V tiles of 64 keys are streamed HBM -> VGPR -> LDS, double
-//     buffered, so the next tile's loads overlap this tile's matrix work;
+//   * K and V tiles of 64 keys are copied HBM -> LDS by DMA
+//     (global_load_lds), double buffered, so the next tile's copy overlaps
+//     this tile's matrix work;
 //   * S^T = K Q^T on MFMA 32x32x16 puts one query per lane (two lanes per
 //     query, 16 keys each), so the row max needs one cross-lane step and the
 //     row sum none until the epilogue;
@@ -48,16 +49,15 @@ struct FwdParams {
 template <int D, int DT, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BR = 128, BC = 64;
-  constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KC = D / 16;               // MFMA steps along D
   constexpr int DB = D / 32;               // 32-wide output blocks along D
   constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
-  constexpr int RPP = 256 / NCH;           // rows per load pass
-  constexpr int PASSES = BC / RPP;
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
+  const uint32_t nb = nat_base<D>(lane);
+  const uint32_t tb = tr_base<D>(lane);
 
   // logical tile id -> (q tile, head, batch)
   const int nwg = p.n_qtiles * p.n_heads * p.n_batch;
@@ -115,40 +115,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    const int lrow = tid / NCH, lch = tid % NCH;
-    u32x4 kpre[PASSES], vpre[PASSES];
-    auto load_tile = [&](int t) {
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const int j = t * BC + lrow + it * RPP;
-        if (j < Sk) {
-          kpre[it] = gload128(kbase + (int64_t)j * p.k_rstride + lch * 8);
-          vpre[it] = gload128(vbase + (int64_t)j * p.k_rstride + lch * 8);
-        } else {
-          kpre[it] = u32x4{0, 0, 0, 0};
-          vpre[it] = u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    auto store_tile = [&](int buf) {
+    auto issue = [&](int t, int buf) {
       char* kt = smem + buf * 2 * TILE;
-      char* vt = kt + TILE;
-#pragma unroll
-      for (int it = 0; it < PASSES; ++it) {
-        const uint32_t o = tile_off<D>(lrow + it * RPP, lch);
-        lds_write128(kt, o, kpre[it]);
-        lds_write128(vt, o, vpre[it]);
-      }
+      dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
 
-    load_tile(t_lo);
-    store_tile(0);
+    issue(t_lo, 0);
+    dma_wait();
     __syncthreads();
 
     for (int t = t_lo; t < t_hi; ++t) {
       const int buf = (t - t_lo) & 1;
-      const bool more = t + 1 < t_hi;
-      if (more) load_tile(t + 1);
+      if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
       const char* kt = smem + buf * 2 * TILE;
       const char* vt = kt + TILE;
       const int j0 = t * BC;
@@ -161,21 +140,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           s[kb] = f32x16{};
 #pragma unroll
           for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_read_nat<D>(kt, kb * 32 + r, 2 * c + g), qreg[c], s[kb]);
+            s[kb] = mfma32<DT>(lds_nat(lds_addr(kt) + nb + (kb * 32) * (D * 2), c), qreg[c], s[kb]);
           }
         }
-        // ---- score transform and mask ----
+        // ---- score transform and mask (keys past Sk hold a copy of the last key) ----
+        if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = s[kb][i];
-            const int j = j0 + 32 * kb + frag_row(i, g);
-            if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
-            else if constexpr (ALIBI) x = x * p.scale_log2;
-            if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
-            if (cls == 1 && !(row_ok && visible(ip, j, Sk, mask))) x = -INFINITY;
-            s[kb][i] = x;
+            for (int i = 0; i < 16; ++i) {
+              float x = s[kb][i];
+              const int j = j0 + 32 * kb + frag_row(i, g);
+              if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
+              else x = x * p.scale_log2;
+              if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
+              s[kb][i] = x;
+            }
+          }
+        }
+        if (cls == 1) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = j0 + 32 * kb + frag_row(i, g);
+              s[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? s[kb][i] : -INFINITY;
+            }
           }
         }
         // ---- online softmax (log2 domain) ----
@@ -209,11 +199,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           const u32x4 pb = pack_frag_half<DT>(s[mk >> 1], mk & 1);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            oacc[d] = mfma32<DT>(lds_read_At<D>(vt, 16 * mk, 32 * d, lane), pb, oacc[d]);
+            oacc[d] = mfma32<DT>(lds_At<D>(lds_addr(vt) + tb + (16 * mk) * (D * 2), d), pb, oacc[d]);
           }
         }
       }
-      if (more) store_tile(buf ^ 1);
+      dma_wait();
       __syncthreads();
     }
   }
