@@ -51,6 +51,9 @@ struct BwdParams {
   int n_tokens;  // preprocess: number of (token) rows
 };
 
+// dK/dV work-group: this many waves of 32 keys each (two waves per SIMD).
+constexpr int DKDV_WAVES = 8;
+
 struct SeqBounds {
   int q_start, Sq, k_start, Sk;
 };
@@ -135,17 +138,23 @@ __device__ __forceinline__ float softcap_grad(float ds, float pv, float x, int i
 }
 
 // --------------------------------------------------------------- dK / dV --
-// Work-group = 128 keys of one K/V head, 4 waves of 32 keys, two work-groups
-// per CU.  Query tiles of 64 rows (Q, dO, LSE, delta) are copied into LDS by
-// DMA, double buffered; the copy of tile n+1 runs under the matrix work of
-// tile n.
+// Work-group = 256 keys of one K/V head, 8 waves of 32 keys (two per SIMD).
+// K rows stay in VGPRs; V rows sit in LDS for the whole kernel (that frees
+// the VGPRs two waves per SIMD need).  Query tiles of 64 rows (Q, dO, LSE,
+// delta) are copied into LDS by DMA, double buffered; the copy of tile n+1
+// runs under the matrix work of tile n.
 template <int D, int DT, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BC = 128, BR = 64;
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = DKDV_WAVES, BC = 32 * NW, BR = 64;
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BR * D * 2;
   constexpr int STAGE = 2 * TILE + 2 * BR * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // V rows of the work-group's keys (B operand of dP = dO V^T), and two stage
+  // buffers, distinct arrays so that reads of one are never ordered behind
+  // the DMA into the other
+  __shared__ __attribute__((aligned(1024))) char vsm[BC * D * 2];
+  __shared__ __attribute__((aligned(1024))) char sm0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
@@ -167,12 +176,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   const bool key_ok = my_key < Sk;
   const int64_t krow = (int64_t)(sb.k_start + my_key) * p.k_rstride + hk * D;
 
-  u32x4 kreg[KC], vreg[KC];
+  u32x4 kreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     kreg[c] = key_ok ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
-    vreg[c] = key_ok ? gload128(p.v + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
+  const char* vw = vsm + (32 * w) * (D * 2);  // this wave's 32 V rows
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
@@ -188,13 +197,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   if (i_lo < i_hi) {
     const int t_lo = i_lo / BR, nt = (i_hi + BR - 1) / BR - t_lo;
     const int n_iter = nt * p.g;
-    auto issue = [&](int n, int buf) {
+    auto issue = [&](int n, char* st) {
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
-      char* st = smem + buf * STAGE;
       const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * D;
-      dma_tile<D, BR, 4>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
-      dma_tile<D, BR, 4>(st + TILE, p.dout + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW>(st + TILE, p.dout + hoff, p.q_rstride, i0, Sq, w, lane);
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
         const int i = min(i0 + lane, Sq - 1);
@@ -202,15 +210,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
 
-    issue(0, 0);
-    dma_wait();
-    __syncthreads();
-    for (int n = 0; n < n_iter; ++n) {
-      const int buf = n & 1;
-      if (n + 1 < n_iter) issue(n + 1, buf ^ 1);
+    // One query tile: `st` holds tile n, `nxt` receives tile n + 1.
+    auto step = [&](const char* st, char* nxt, int n) {
+      if (n + 1 < n_iter) issue(n + 1, nxt);
+      const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
-      const char* st = smem + buf * STAGE;
       const char* qt = st;
       const char* dot = st + TILE;
       const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
@@ -228,8 +233,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          s = mfma32<DT>(lds_nat(lds_addr(qt) + nb + (32 * rb) * (D * 2), c), kreg[c], s);
-          dp = mfma32<DT>(lds_nat(lds_addr(dot) + nb + (32 * rb) * (D * 2), c), vreg[c], dp);
+          s = mfma32<DT>(lds_nat(qt + (32 * rb) * (D * 2), nbv, c), kreg[c], s);
+          dp = mfma32<DT>(lds_nat(dot + (32 * rb) * (D * 2), nbv, c), lds_nat(vw, nbv, c), dp);
         }
         // logits, mask (rows past Sq hold a copy of the last row), P and dS
         if constexpr (SOFTCAP || ALIBI) {
@@ -270,14 +275,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
           const u32x4 sb2 = pack_frag_half<DT>(dp, mk);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            dvacc[d] = mfma32<DT>(lds_At<D>(lds_addr(dot) + tb + (32 * rb + 16 * mk) * (D * 2), d), pb, dvacc[d]);
-            dkacc[d] = mfma32<DT>(lds_At<D>(lds_addr(qt) + tb + (32 * rb + 16 * mk) * (D * 2), d), sb2, dkacc[d]);
+            dvacc[d] = mfma32<DT>(lds_At<D>(dot + (32 * rb + 16 * mk) * (D * 2), tbv, d), pb, dvacc[d]);
+            dkacc[d] = mfma32<DT>(lds_At<D>(qt + (32 * rb + 16 * mk) * (D * 2), tbv, d), sb2, dkacc[d]);
           }
         }
       }
       dma_wait();
       __syncthreads();
+    };
+
+    // V rows past Sk hold a copy of the last row; their keys are masked
+    dma_tile<D, BC, NW>(vsm, p.v + (int64_t)sb.k_start * p.k_rstride + hk * D, p.k_rstride, k0, Sk, w, lane);
+    issue(0, sm0);
+    dma_wait();
+    __syncthreads();
+    int n = 0;
+    for (; n + 1 < n_iter; n += 2) {
+      step(sm0, sm1, n);
+      step(sm1, sm0, n + 1);
     }
+    if (n < n_iter) step(sm0, sm1, n);
   }
 
   if (key_ok) {
@@ -308,7 +325,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BC * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  // two stage buffers (K tile then V tile), distinct arrays so that reads of
+  // one are never ordered behind the DMA into the other
+  __shared__ __attribute__((aligned(1024))) char sm0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char sm1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
@@ -362,18 +382,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    auto issue = [&](int t, int buf) {
-      char* kt = smem + buf * 2 * TILE;
+    auto issue = [&](int t, char* kt) {
       dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
       dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
-    issue(t_lo, 0);
-    dma_wait();
-    __syncthreads();
-    for (int t = t_lo; t < t_hi; ++t) {
-      const int buf = (t - t_lo) & 1;
-      if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
-      const char* kt = smem + buf * 2 * TILE;
+    // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
+    auto step = [&](const char* kt, char* nxt, int t) {
+      if (t + 1 < t_hi) issue(t + 1, nxt);
+      const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const char* vt = kt + TILE;
       const int j0 = t * BC;
       // keys past the end hold a copy of the last key: classify marks such tiles partial
@@ -386,8 +402,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
           dp[kb] = f32x16{};
 #pragma unroll
           for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_nat(lds_addr(kt) + nb + (kb * 32) * (D * 2), c), qreg[c], s[kb]);
-            dp[kb] = mfma32<DT>(lds_nat(lds_addr(vt) + nb + (kb * 32) * (D * 2), c), doreg[c], dp[kb]);
+            s[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], s[kb]);
+            dp[kb] = mfma32<DT>(lds_nat(vt + (kb * 32) * (D * 2), nbv, c), doreg[c], dp[kb]);
           }
         }
         // logits, mask (keys past Sk hold a copy of the last key), P and dS
@@ -427,13 +443,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
           const u32x4 db = pack_frag_half<DT>(dp[mk >> 1], mk & 1);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            dqacc[d] = mfma32<DT>(lds_At<D>(lds_addr(kt) + tb + (16 * mk) * (D * 2), d), db, dqacc[d]);
+            dqacc[d] = mfma32<DT>(lds_At<D>(kt + (16 * mk) * (D * 2), tbv, d), db, dqacc[d]);
           }
         }
       }
       dma_wait();
       __syncthreads();
+    };
+
+    issue(t_lo, sm0);
+    dma_wait();
+    __syncthreads();
+    int t = t_lo;
+    for (; t + 1 < t_hi; t += 2) {
+      step(sm0, sm1, t);
+      step(sm1, sm0, t + 1);
     }
+    if (t < t_hi) step(sm0, sm1, t);
   }
 
   if (row_ok) {
@@ -456,7 +482,7 @@ template <int D, int DT, bool SC, bool AL>
 static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
   if (nwg_kv > 0) {
     prof_before(FA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL>), dim3(nwg_kv), dim3(256), 0, st, dkdv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL>), dim3(nwg_kv), dim3(64 * DKDV_WAVES), 0, st, dkdv);
     prof_after(FA_KERNEL_BWD_DKDV, st);
   }
   if (nwg_q > 0) {
@@ -491,7 +517,7 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   const long long pre_threads = (long long)n_tokens * base.Hq * (D / 8);
   const long long nwg_pre = (pre_threads + 255) / 256;
   BwdParams kv = base;
-  kv.n_tiles = (max_sk + 127) / 128;
+  kv.n_tiles = (max_sk + 32 * DKDV_WAVES - 1) / (32 * DKDV_WAVES);
   kv.n_heads = Hkv;
   kv.n_batch = nbatch;
   kv.reverse = 0;

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
       for (int mk = 0; mk < 2; ++mk) {
         const u32x4 pb = pack_frag_half<DT>(s, mk);
 #pragma unroll
-        for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_At<D>(lds_addr(vt) + tb + (16 * mk) * (D * 2), d), pb, oacc[d]);
+        for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tb, d), pb, oacc[d]);
       }
     }
   }

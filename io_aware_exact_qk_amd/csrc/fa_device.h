@@ -169,18 +169,13 @@ __device__ __forceinline__ uint32_t row_base(int row) {
   return (uint32_t)row * (D * 2) + (swz<D>(row) << 4);
 }
 
-// 32-bit LDS byte address of a pointer into __shared__ memory, and reads at
-// such addresses.
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
-__device__ __forceinline__ u32x4 lds_ld128(uint32_t a) { return *(const lds_u32x4*)a; }
-__device__ __forceinline__ u32x2 lds_ld_tr(uint32_t a) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a));
+// A value the compiler must treat as redefined at this point.  Loop bodies
+// pass their per-lane LDS offsets through it once per iteration, so the
+// per-read XORs below are recomputed in the loop (one VALU each) instead of
+// being hoisted into one live register per read.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Natural-order operand offset of a lane: row r = lane % 32 of a 32-row block,
@@ -191,11 +186,13 @@ __device__ __forceinline__ uint32_t nat_base(int lane) {
 }
 
 // Step c (16 contraction elements: chunks 2c and 2c + 1) of a natural-order
-// operand.  `a` = LDS address of the operand's first row (256-byte aligned,
-// 16-row aligned within its tile) + the lane's nat_base.  The XOR is applied
-// after the per-iteration tile address is added, so no per-step address is
-// held in a register across the loop.
-__device__ __forceinline__ u32x4 lds_nat(uint32_t a, int c) { return lds_ld128(a ^ ((uint32_t)c << 5)); }
+// operand whose 32 rows start at `tile` (16-row aligned within its tile);
+// nb = the lane's nat_base.  Addresses stay derived from the __shared__ array
+// (no integer-to-pointer casts), so the compiler can tell a read of one stage
+// buffer from a DMA into the other and does not wait for that DMA.
+__device__ __forceinline__ u32x4 lds_nat(const char* tile, uint32_t nb, int c) {
+  return lds_read128(tile, nb ^ ((uint32_t)c << 5));
+}
 
 // Transposed (acc-order) operand offset of a lane for lds_At: byte offset,
 // relative to a 16-row-aligned row0, of the 4-element piece it fetches from
@@ -211,13 +208,13 @@ __device__ __forceinline__ uint32_t tr_base(int lane) {
 }
 
 // A operand (32 x 16) whose 32 rows are tile columns 32d .. 32d+31 and whose
-// contraction runs over 16 tile rows.  `a` = LDS address of the first of those
-// rows (256-byte aligned, 16-row aligned within its tile) + the lane's tr_base.
+// contraction runs over the 16 tile rows starting at `tile` (16-row aligned);
+// tb = the lane's tr_base.
 template <int D>
-__device__ __forceinline__ u32x4 lds_At(uint32_t a, int d) {
-  const uint32_t lo = a ^ ((uint32_t)d << 6);  // column block d = chunks 4d .. 4d+3
-  const u32x2 x = lds_ld_tr(lo);
-  const u32x2 y = lds_ld_tr((lo ^ 32u) + 8 * (D * 2));
+__device__ __forceinline__ u32x4 lds_At(const char* tile, uint32_t tb, int d) {
+  const uint32_t lo = tb ^ ((uint32_t)d << 6);  // column block d = chunks 4d .. 4d+3
+  const u32x2 x = lds_read_tr(tile, lo);
+  const u32x2 y = lds_read_tr(tile + 8 * (D * 2), lo ^ 32u);
   u32x4 out = {x[0], x[1], y[0], y[1]};
   return out;
 }

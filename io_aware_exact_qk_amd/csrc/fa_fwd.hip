@@ -52,7 +52,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int KC = D / 16;               // MFMA steps along D
   constexpr int DB = D / 32;               // 32-wide output blocks along D
   constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  // two stage buffers (K tile then V tile), distinct arrays so that reads of
+  // one are never ordered behind the DMA into the other
+  __shared__ __attribute__((aligned(1024))) char sm0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char sm1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
@@ -115,20 +118,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    auto issue = [&](int t, int buf) {
-      char* kt = smem + buf * 2 * TILE;
+    auto issue = [&](int t, char* kt) {
       dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
       dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
 
-    issue(t_lo, 0);
-    dma_wait();
-    __syncthreads();
-
-    for (int t = t_lo; t < t_hi; ++t) {
-      const int buf = (t - t_lo) & 1;
-      if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
-      const char* kt = smem + buf * 2 * TILE;
+    // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
+    auto step = [&](const char* kt, char* nxt, int t) {
+      if (t + 1 < t_hi) issue(t + 1, nxt);
+      const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const char* vt = kt + TILE;
       const int j0 = t * BC;
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           s[kb] = f32x16{};
 #pragma unroll
           for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_nat(lds_addr(kt) + nb + (kb * 32) * (D * 2), c), qreg[c], s[kb]);
+            s[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], s[kb]);
           }
         }
         // ---- score transform and mask (keys past Sk hold a copy of the last key) ----
@@ -199,13 +197,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           const u32x4 pb = pack_frag_half<DT>(s[mk >> 1], mk & 1);
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            oacc[d] = mfma32<DT>(lds_At<D>(lds_addr(vt) + tb + (16 * mk) * (D * 2), d), pb, oacc[d]);
+            oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tbv, d), pb, oacc[d]);
           }
         }
       }
       dma_wait();
       __syncthreads();
+    };
+
+    issue(t_lo, sm0);
+    dma_wait();
+    __syncthreads();
+    int t = t_lo;
+    for (; t + 1 < t_hi; t += 2) {
+      step(sm0, sm1, t);
+      step(sm1, sm0, t + 1);
     }
+    if (t < t_hi) step(sm0, sm1, t);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
