@@ -39,6 +39,9 @@ enum { DT_F16 = 0, DT_BF16 = 1 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax: how far (log2 units) a row max may exceed the exponent
+// reference before the accumulators are rescaled.
+constexpr float kRescaleSlack = 8.0f;
 
 // ---------------------------------------------------------------- MFMA ----
 template <int DT>

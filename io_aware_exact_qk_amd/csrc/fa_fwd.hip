@@ -10,8 +10,11 @@
 //   * each wave owns 32 query rows; their Q fragment stays in VGPRs for the
 //     whole key loop (B operand of S^T = K Q^T);
 //   * K and V tiles of 64 keys are copied HBM -> LDS by DMA
-//     (global_load_lds), double buffered, so the next tile's copy overlaps
-//     this tile's matrix work;
+//     (global_load_lds) into separate double buffers; the copies of K for
+//     tile t+2 and V for tile t+1 overlap the work on tile t;
+//   * the key loop is software pipelined: the MFMAs of S for tile t+1 are
+//     issued in the same basic block as the exponentials of tile t, so one
+//     wave keeps the matrix core busy while its VALU does the softmax;
 //   * S^T = K Q^T on MFMA 32x32x16 puts one query per lane (two lanes per
 //     query, 16 keys each), so the row max needs one cross-lane step and the
 //     row sum none until the epilogue;
@@ -52,10 +55,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int KC = D / 16;               // MFMA steps along D
   constexpr int DB = D / 32;               // 32-wide output blocks along D
   constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
-  // two stage buffers (K tile then V tile), distinct arrays so that reads of
-  // one are never ordered behind the DMA into the other
-  __shared__ __attribute__((aligned(1024))) char sm0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) char sm1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
@@ -118,102 +121,148 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    auto issue = [&](int t, char* kt) {
-      dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
-      dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
+    auto dma_k = [&](int t, char* dst) { dma_tile<D, BC, 4>(dst, kbase, p.k_rstride, t * BC, Sk, w, lane); };
+    auto dma_v = [&](int t, char* dst) { dma_tile<D, BC, 4>(dst, vbase, p.k_rstride, t * BC, Sk, w, lane); };
+
+    // S^T = K Q^T for the 64 keys of LDS tile `kt` (raw dot products).
+    auto qk = [&](const char* kt, uint32_t nbv, f32x16 (&sa)[2]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sa[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          sa[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], sa[kb]);
+        }
+      }
     };
 
-    // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
-    auto step = [&](const char* kt, char* nxt, int t) {
-      if (t + 1 < t_hi) issue(t + 1, nxt);
-      const uint32_t nbv = opaque(nb), tbv = opaque(tb);
-      const char* vt = kt + TILE;
+    // Logits of tile t in the log2 domain (up to the folded scale fs), masked
+    // entries at -inf (keys past Sk hold a copy of the last key), then the
+    // lazy online-softmax update of the exponent reference.  Returns m_use.
+    auto prep = [&](int t, f32x16 (&sa)[2]) -> float {
       const int j0 = t * BC;
-      const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
-      if (cls != 0) {
-        // ---- S^T = K Q^T for 64 keys x 32 queries ----
-        f32x16 s[2];
+      if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], s[kb]);
-          }
-        }
-        // ---- score transform and mask (keys past Sk hold a copy of the last key) ----
-        if constexpr (SOFTCAP || ALIBI) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float x = s[kb][i];
-              const int j = j0 + 32 * kb + frag_row(i, g);
-              if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
-              else x = x * p.scale_log2;
-              if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
-              s[kb][i] = x;
-            }
-          }
-        }
-        if (cls == 1) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = j0 + 32 * kb + frag_row(i, g);
-              s[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? s[kb][i] : -INFINITY;
-            }
-          }
-        }
-        // ---- online softmax (log2 domain) ----
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx * fs);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float lsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float pv = fast_exp2(fmaf(s[kb][i], fs, -m_use));
-            s[kb][i] = pv;
-            lsum += pv;
-          }
-        l_run = fmaf(l_run, alpha, lsum);
-        m_run = m_new;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
-        }
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int mk = 0; mk < 4; ++mk) {
-          const u32x4 pb = pack_frag_half<DT>(s[mk >> 1], mk & 1);
-#pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tbv, d), pb, oacc[d]);
+            float x = sa[kb][i];
+            const int j = j0 + 32 * kb + frag_row(i, g);
+            if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
+            else x = x * p.scale_log2;
+            if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
+            sa[kb][i] = x;
           }
         }
       }
+      const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
+      if (cls != 2) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * kb + frag_row(i, g);
+            sa[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? sa[kb][i] : -INFINITY;
+          }
+        }
+      }
+      // The exponent reference m_run moves only when the tile max exceeds it
+      // by more than kRescaleSlack; until then p <= 2^kRescaleSlack, which the
+      // float32 sums and the 16-bit P operand carry without loss, and the
+      // rescale of O (64 multiplies per lane) is skipped.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[kb][i]);
+      mx = fmaxf(mx, xor32(mx)) * fs;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      return (m_run == -INFINITY) ? 0.0f : m_run;
+    };
+
+    // P = 2^(x - m) as four 16-bit B operands (acc-order), row sums into l_run.
+    auto expo = [&](f32x16 (&sa)[2], float m_use, u32x4 (&pb)[4]) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(fmaf(sa[kb][i], fs, -m_use));
+          sa[kb][i] = pv;
+          lsum += pv;
+        }
+      l_run += lsum;
+#pragma unroll
+      for (int mk = 0; mk < 4; ++mk) pb[mk] = pack_frag_half<DT>(sa[mk >> 1], mk & 1);
+    };
+
+    // O^T += V^T P^T over the 64 keys of LDS tile `vt`.
+    auto pv = [&](const char* vt, uint32_t tbv, const u32x4 (&pb)[4]) {
+#pragma unroll
+      for (int mk = 0; mk < 4; ++mk) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tbv, d), pb[mk], oacc[d]);
+        }
+      }
+    };
+
+    // Pipelined step for tile t (t + 1 < t_hi): `sc` holds S of tile t, the
+    // MFMAs of S for tile t + 1 (K in `kn`, into `sn`) run in the same basic
+    // block as the exponentials of tile t, then O += P V with V of tile t in
+    // `vt`.  DMA: K of tile t + 2 into `kdst` (K of tile t, already used),
+    // V of tile t + 1 into `vdst` (V of tile t - 1, already used).
+    auto step = [&](int t, const char* kn, const char* vt, char* kdst, char* vdst, f32x16 (&sc)[2],
+                    f32x16 (&sn)[2]) {
+      if (t + 2 < t_hi) dma_k(t + 2, kdst);
+      dma_v(t + 1, vdst);
+      const uint32_t nbv = opaque(nb), tbv = opaque(tb);
+      const float m_use = prep(t, sc);
+      u32x4 pb[4];
+      qk(kn, nbv, sn);
+      expo(sc, m_use, pb);
+      pv(vt, tbv, pb);
       dma_wait();
       __syncthreads();
     };
 
-    issue(t_lo, sm0);
+    // Final tile: no next S, no DMA.
+    auto last = [&](int t, const char* vt, f32x16 (&sc)[2]) {
+      const uint32_t tbv = opaque(tb);
+      const float m_use = prep(t, sc);
+      u32x4 pb[4];
+      expo(sc, m_use, pb);
+      pv(vt, tbv, pb);
+    };
+
+    // Four distinct LDS arrays: K and V, double buffered, so reads of one are
+    // never ordered behind the DMA into another.
+    f32x16 sA[2], sB[2];
+    dma_k(t_lo, kb0);
+    dma_v(t_lo, vb0);
+    if (t_lo + 1 < t_hi) dma_k(t_lo + 1, kb1);
     dma_wait();
     __syncthreads();
+    qk(kb0, nb, sA);
+    __syncthreads();  // every wave is done with kb0 before it is refilled
     int t = t_lo;
-    for (; t + 1 < t_hi; t += 2) {
-      step(sm0, sm1, t);
-      step(sm1, sm0, t + 1);
+    for (; t + 2 < t_hi; t += 2) {
+      step(t, kb1, vb0, kb0, vb1, sA, sB);
+      step(t + 1, kb0, vb1, kb1, vb0, sB, sA);
     }
-    if (t < t_hi) step(sm0, sm1, t);
+    if (t + 1 < t_hi) {
+      step(t, kb1, vb0, kb0, vb1, sA, sB);
+      last(t + 1, vb1, sB);
+    } else {
+      last(t, vb0, sA);
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
