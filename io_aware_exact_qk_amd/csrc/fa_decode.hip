@@ -8,19 +8,26 @@
 // to balance latency for small batches with long contexts.
 //
 // Split kernel: one work-group per (sequence, K/V head, split).  A split is a
-// contiguous range of pages.  Its 4 waves take 32-key tiles round robin:
-//   * the K tile goes HBM -> VGPR straight into the A operand of
-//     S^T = K Q^T (one key row per lane, natural order);
+// contiguous range of pages.  The path is bound by HBM bandwidth, so the
+// kernel runs one wave per SIMD and spends its registers and LDS on bytes in
+// flight.  Its 4 waves take 32-key tiles round robin, each wave streaming
+// its own tiles with no work-group barrier:
+//   * K rows go HBM -> VGPR straight into the A operand of S^T = K Q^T (one
+//     key row per lane, natural order); V rows go HBM -> LDS by DMA into a
+//     wave-private tile and are read back transposed as the A operand of
+//     O^T += V^T P^T;
+//   * four stages: while a tile is computed, the next three tiles' loads
+//     are in flight (48 KB per wave);
 //   * all query heads of the group (Hq / Hkv <= 32) are the 32 columns of the
 //     B operand, so every K/V byte is read once for the whole group;
 //   * the rotated query is split into a 16-bit high part and a 16-bit
 //     remainder and both are multiplied, so rounding the rotated query to
 //     16 bits costs no accuracy in the scores;
-//   * V goes through a wave-private LDS tile and is read back transposed as
-//     the A operand of O^T += V^T P^T;
-//   * the tile holding position cache_seqlens[b] takes the rotated k_new and
-//     v_new from registers and the same lanes write them to the cache slot,
-//     so no other work-group ever reads that slot.
+//   * the wave whose tiles include position cache_seqlens[b] rotates k_new,
+//     writes it and v_new to the cache slot in its prologue and patches them
+//     into that tile, so no other work-group ever reads that slot;
+//   * sequences are served longest cache first, which keeps the tail short
+//     when lengths differ.
 // The 4 waves' (max, sum, O) states are merged exactly in LDS.  With one
 // split the kernel writes the final output; otherwise it writes float32
 // partials (O_s normalised, LSE_s) that the combine kernel merges with
@@ -50,35 +57,6 @@ struct DecParams {
   float scale_log2;
 };
 
-// Rotated 8-element chunk `ch` of a row (16-bit storage) as 8 floats.
-template <int D, int DT>
-__device__ __forceinline__ void rotate_chunk(const uint16_t* row, int ch, int pos, const DecParams& p, float out[8]) {
-  const u32x4 a = gload128(row + ch * 8);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    out[2 * e] = to_f32<DT>((uint16_t)(a[e] & 0xffff));
-    out[2 * e + 1] = to_f32<DT>((uint16_t)(a[e] >> 16));
-  }
-  const int rd = p.rotary_dim;
-  if (rd == 0 || p.cos == nullptr) return;
-  const int half = rd / 2;
-  const int d0 = ch * 8;
-  if (d0 >= rd) return;
-  const bool first = d0 < half;
-  const int pch = first ? ch + half / 8 : ch - half / 8;
-  const u32x4 b = gload128(row + pch * 8);
-  const int fi0 = first ? d0 : d0 - half;  // frequency index of element 0
-  const float* cr = p.cos + (int64_t)pos * half + fi0;
-  const float* sr = p.sin + (int64_t)pos * half + fi0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t pb = (uint16_t)((e & 1) ? (b[e >> 1] >> 16) : (b[e >> 1] & 0xffff));
-    const float y = to_f32<DT>(pb);
-    const float c = cr[e], s = sr[e];
-    out[e] = first ? (out[e] * c - y * s) : (out[e] * c + y * s);
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ u32x4 pack8(const float x[8]) {
   u32x4 r;
@@ -92,21 +70,61 @@ __device__ __forceinline__ float lo16(uint32_t v) { return to_f32<DT>((uint16_t)
 template <int DT>
 __device__ __forceinline__ float hi16(uint32_t v) { return to_f32<DT>((uint16_t)(v >> 16)); }
 
+typedef __attribute__((address_space(4))) const int cint;  // constant address space
+
+// Batches up to this size are scheduled longest cache first.
+constexpr int kDecodeSortMax = 64;
+
 template <int D, int DT>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
+__global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int BK = 32;  // keys per wave tile
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int VT = BK * D * 2;  // bytes of one wave's V tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * VT + 2 * 4 * 32 * 4];
+  constexpr int NVM = KC + VT / 1024;  // vector-memory instructions per tile load
+  // V tiles, one per wave and stage; four distinct arrays (one per stage) so
+  // a read of one stage is never ordered behind the DMA into another.
+  __shared__ __attribute__((aligned(1024))) char vs0[4 * VT];
+  __shared__ __attribute__((aligned(1024))) char vs1[4 * VT];
+  __shared__ __attribute__((aligned(1024))) char vs2[4 * VT];
+  __shared__ __attribute__((aligned(1024))) char vs3[4 * VT];
+  __shared__ float mbuf[4 * 32], lbuf[4 * 32];
+  __shared__ __attribute__((aligned(16))) char apbuf[4 * D];  // rotated k_new row, v_new row
+  __shared__ __attribute__((aligned(16))) char qst[33 * D * 2];  // query rows (G <= 32), k_new row
+  __shared__ float rot_cs[D];                                     // cos, sin at position L
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int hf = lane >> 5, r = lane & 31;
   const uint32_t tb = tr_base<D>(lane);
   const int s_id = blockIdx.x % p.num_splits;
   const int hkv = (blockIdx.x / p.num_splits) % p.Hkv;
-  const int b = blockIdx.x / (p.num_splits * p.Hkv);
+  const int rank = blockIdx.x / (p.num_splits * p.Hkv);
+  // Work-groups are dispatched roughly in id order and one fits per CU, so
+  // the sequences are taken longest cache first (ties by index): the rank-th
+  // id group serves the sequence whose length has that rank.  Integer work
+  // only; every work-group computes the same permutation.
+  __shared__ int sel_b;
+  int b = rank;
+  if (p.B <= kDecodeSortMax) {
+    for (int bb = tid; bb < p.B; bb += 256) {
+      const int lb = p.cache_seqlens[bb];
+      int rk = 0;
+      for (int o = 0; o < p.B; ++o) {
+        const int lo = p.cache_seqlens[o];
+        rk += (lo > lb) | ((lo == lb) & (o < bb));
+      }
+      if (rk == rank) sel_b = bb;
+    }
+    __syncthreads();
+    b = sel_b;
+  }
 
-  const int L = p.cache_seqlens[b];
+  // b and every index derived from it are wave-uniform; reading the cache
+  // lengths and the block table through the constant address space makes
+  // them scalar loads, which the vector-memory counter of the K/V stream
+  // does not have to drain.
+  b = __builtin_amdgcn_readfirstlane(b);
+  const int L = ((const cint*)p.cache_seqlens)[b];
   const bool append = p.k_new != nullptr;
   const int n_keys = L + (append ? 1 : 0);
   const int page = p.page_size;
@@ -117,16 +135,61 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
   const int k_lo = p_lo * page;
   const int k_hi = min(p_hi * page, n_keys);
 
+  // ---- stage the group's query rows, the k_new row and the rotary row of
+  // position L in LDS with independent loads (one round trip) ----
+  constexpr int NCH = D / 8;
+  const int hr = p.cos ? p.rotary_dim / 2 : 0;  // rotary half width (0 = off)
+  {
+    const int nq = p.G * NCH, nk = append ? NCH : 0;
+    const int total = nq + nk + 2 * hr;
+    for (int i = tid; i < total; i += 256) {
+      if (i < nq) {
+        const int row = i / NCH, ch = i % NCH;
+        const u32x4 v = gload128(p.q + ((int64_t)b * p.Hq + hkv * p.G + row) * D + ch * 8);
+        lds_write128(qst, (row * D + ch * 8) * 2, v);
+      } else if (i < nq + nk) {
+        const int ch = i - nq;
+        const u32x4 v = gload128(p.k_new + ((int64_t)b * p.Hkv + hkv) * D + ch * 8);
+        lds_write128(qst, (32 * D + ch * 8) * 2, v);
+      } else {
+        const int j = i - nq - nk;  // cos[0..hr) then sin[0..hr) at position L
+        rot_cs[j] = j < hr ? p.cos[(int64_t)L * hr + j] : p.sin[(int64_t)L * hr + (j - hr)];
+      }
+    }
+    __syncthreads();
+  }
+  // Chunk ch (8 elements) of a staged row, rotated at position L: the
+  // half-split pairs (x_i, x_{i+hr}) for i < hr; dims >= 2 hr pass through.
+  auto rot8 = [&](const char* row, int ch, float x[8]) {
+    const u32x4 a = lds_read128(row, ch * 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = lo16<DT>(a[e]);
+      x[2 * e + 1] = hi16<DT>(a[e]);
+    }
+    const int d0 = 8 * ch;
+    if (d0 < 2 * hr) {
+      const bool first = d0 < hr;
+      const int pch = first ? ch + hr / 8 : ch - hr / 8;
+      const int fi0 = first ? d0 : d0 - hr;
+      const u32x4 bv = lds_read128(row, pch * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = (e & 1) ? hi16<DT>(bv[e >> 1]) : lo16<DT>(bv[e >> 1]);
+        const float c = rot_cs[fi0 + e], sn = rot_cs[hr + fi0 + e];
+        x[e] = first ? (x[e] * c - y * sn) : (x[e] * c + y * sn);
+      }
+    }
+  };
+
   // ---- query fragment (B operand, column = query head of the group) ----
-  const int hq = hkv * p.G + r;
   const bool col_ok = r < p.G;
-  const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + hq) * D;
   u32x4 qhi[KC], qlo[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     if (col_ok) {
       float x[8], rem[8];
-      rotate_chunk<D, DT>(qrow, 2 * c + hf, L, p, x);
+      rot8(qst + r * (D * 2), 2 * c + hf, x);
       qhi[c] = pack8<DT>(x);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -144,112 +207,167 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
-  char* vt = smem + w * VT;
 
-  if (k_lo < k_hi) {
-    const int t_lo = k_lo / BK, t_hi = (k_hi + BK - 1) / BK;
-    const int64_t cap = (int64_t)p.max_blocks * page;
-    for (int t = t_lo + w; t < t_hi; t += 4) {
-      const int j0 = t * BK;
-      const int j = j0 + r;  // key row this lane loads
-      int64_t rowoff = 0;
-      if (p.block_table) {
-        const int phys = p.block_table[(int64_t)b * p.max_blocks + j0 / page];
-        rowoff = (((int64_t)phys * page + (j % page)) * p.Hkv + hkv) * D;
-      } else {
-        rowoff = (((int64_t)b * cap + j) * p.Hkv + hkv) * D;
-      }
-      u32x4 ka[KC], va[KC];
-      if (append && j == L) {
-        const uint16_t* knr = p.k_new + ((int64_t)b * p.Hkv + hkv) * D;
-        const uint16_t* vnr = p.v_new + ((int64_t)b * p.Hkv + hkv) * D;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          float x[8];
-          rotate_chunk<D, DT>(knr, 2 * c + hf, L, p, x);
-          ka[c] = pack8<DT>(x);
-          va[c] = gload128(vnr + (2 * c + hf) * 8);
-          gstore128(p.k_cache + rowoff + (2 * c + hf) * 8, ka[c]);
-          gstore128(p.v_cache + rowoff + (2 * c + hf) * 8, va[c]);
-        }
-      } else if (j < n_keys) {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          ka[c] = gload128(p.k_cache + rowoff + (2 * c + hf) * 8);
-          va[c] = gload128(p.v_cache + rowoff + (2 * c + hf) * 8);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          ka[c] = u32x4{0, 0, 0, 0};
-          va[c] = u32x4{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < KC; ++c) lds_write128(vt, tile_off<D>(r, 2 * c + hf), va[c]);
-      asm volatile("" ::: "memory");  // the wave reads its own V tile below
+  // Element offset of the first row of the 32-key tile starting at key j0
+  // (a tile never crosses a page: page_size is a multiple of 32).  Rows of
+  // a tile are Hkv * D elements apart.
+  const int64_t cap = (int64_t)p.max_blocks * page;
+  auto tile_base = [&](int j0) -> int64_t {
+    if (p.block_table) {
+      const int phys = ((const cint*)p.block_table)[(int64_t)b * p.max_blocks + j0 / page];
+      return (((int64_t)phys * page + (j0 % page)) * p.Hkv + hkv) * D;
+    }
+    return (((int64_t)b * cap + j0) * p.Hkv + hkv) * D;
+  };
+  const int64_t kvstride = (int64_t)p.Hkv * D;
 
-      f32x16 s = f32x16{};
+  // Tiles of this split, dealt round robin to the 4 waves.
+  const int t_lo = k_lo / BK, t_hi = (k_hi + BK - 1) / BK;
+  const int t_first = t_lo + w;
+  const int n_my = (k_lo < k_hi && t_first < t_hi) ? (t_hi - t_first + 3) / 4 : 0;
+
+  // K rows go straight into VGPRs in A-operand (natural) order; V rows go by
+  // DMA into this wave's LDS tile for the transposed reads.
+  auto load = [&](int t, u32x4 (&ka)[KC], char* vdst) {
+    const int64_t base = tile_base(t * BK);
+    const uint16_t* krow = p.k_cache + base + (int64_t)r * kvstride;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        s = mfma32<DT>(ka[c], qhi[c], s);
-        s = mfma32<DT>(ka[c], qlo[c], s);
-      }
-      const bool ragged = j0 + BK > n_keys;
-      float mx = -INFINITY;
+    for (int c = 0; c < KC; ++c) ka[c] = gload128(krow + (2 * c + hf) * 8);
+    dma_tile<D, BK, 1>(vdst, p.v_cache + base, kvstride, 0, BK, 0, lane);
+  };
+
+  // One tile: `ka` / `vt` hold K and V of tile t.
+  auto compute = [&](int t, u32x4 (&ka)[KC], char* vt) {
+    const int j0 = t * BK;
+    if (append && L >= j0 && L < j0 + BK) {
+      // This tile holds the appended position: its row takes the rotated
+      // k_new and v_new parked in LDS by the prologue instead of the stale
+      // cache row that was streamed in.
+      if (r == L - j0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (ragged && j0 + frag_row(i, hf) >= n_keys) s[i] = -INFINITY;
-        mx = fmaxf(mx, s[i]);
-      }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * p.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[i], p.scale_log2, -m_use));
-        s[i] = pv;
-        lsum += pv;
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
-#pragma unroll
-      for (int mk = 0; mk < 2; ++mk) {
-        const u32x4 pb = pack_frag_half<DT>(s, mk);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tb, d), pb, oacc[d]);
+        for (int c = 0; c < KC; ++c) {
+          ka[c] = lds_read128(apbuf, (2 * c + hf) * 16);
+          lds_write128(vt, tile_off<D>(r, 2 * c + hf), lds_read128(apbuf + 2 * D, (2 * c + hf) * 16));
+        }
       }
     }
+    // two independent accumulation chains (high and low query part): one
+    // wave per SIMD has no other wave to hide a single chain's MFMA latency
+    f32x16 s = f32x16{}, sl = f32x16{};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      s = mfma32<DT>(ka[c], qhi[c], s);
+      sl = mfma32<DT>(ka[c], qlo[c], sl);
+    }
+    s += sl;
+    if (j0 + BK > n_keys) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = (j0 + frag_row(i, hf) < n_keys) ? s[i] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = fast_exp2(fmaf(s[i], p.scale_log2, -m_use));
+      s[i] = pv;
+      lsum += pv;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk) {
+      const u32x4 pb = pack_frag_half<DT>(s, mk);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) oacc[d] = mfma32<DT>(lds_At<D>(vt + (16 * mk) * (D * 2), tb, d), pb, oacc[d]);
+    }
+  };
+
+  // Append (once per call): the wave whose tiles include position L rotates
+  // k_new, writes the rotated key and v_new to the cache slot (no other
+  // wave or work-group reads that slot) and parks both rows in LDS for the
+  // tile that uses them.
+  if (append && L >= k_lo && L < k_hi && ((L / BK - t_lo) & 3) == w && r == L % BK) {
+    const uint16_t* vnr = p.v_new + ((int64_t)b * p.Hkv + hkv) * D;
+    const int64_t slot = tile_base(L - L % BK) + (int64_t)r * kvstride;
+    u32x4 vv[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) vv[c] = gload128(vnr + (2 * c + hf) * 8);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      float x[8];
+      rot8(qst + 32 * (D * 2), 2 * c + hf, x);
+      const u32x4 kk = pack8<DT>(x);
+      gstore128(p.k_cache + slot + (2 * c + hf) * 8, kk);
+      gstore128(p.v_cache + slot + (2 * c + hf) * 8, vv[c]);
+      lds_write128(apbuf, (2 * c + hf) * 16, kk);
+      lds_write128(apbuf + 2 * D, (2 * c + hf) * 16, vv[c]);
+    }
+  }
+  // (the stores above retire before the stream's first wait; they are older
+  // than every tile load)
+
+  // Four-stage stream: while tile i is computed, tiles i+1 .. i+3 are in
+  // flight.  VMEM operations retire in order, so waiting until only the
+  // later tiles' NVM operations each are outstanding completes tile i.
+  char* v0 = vs0 + w * VT;
+  char* v1 = vs1 + w * VT;
+  char* v2 = vs2 + w * VT;
+  char* v3 = vs3 + w * VT;
+  u32x4 k0[KC], k1[KC], k2[KC], k3[KC];
+  auto stage = [&](int i, u32x4 (&kc)[KC], char* vc, u32x4 (&kn)[KC], char* vn) {
+    const int t = t_first + 4 * i;
+    if (i + 3 < n_my) load(t + 12, kn, vn);
+    asm volatile("" ::: "memory");
+    const int later = min(3, n_my - 1 - i);
+    if (later == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NVM));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NVM));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NVM));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    compute(t, kc, vc);
+  };
+  if (n_my > 0) load(t_first, k0, v0);
+  if (n_my > 1) load(t_first + 4, k1, v1);
+  if (n_my > 2) load(t_first + 8, k2, v2);
+  for (int i = 0; i < n_my; i += 4) {
+    stage(i, k0, v0, k3, v3);
+    if (i + 1 < n_my) stage(i + 1, k1, v1, k0, v0);
+    if (i + 2 < n_my) stage(i + 2, k2, v2, k1, v1);
+    if (i + 3 < n_my) stage(i + 3, k3, v3, k2, v2);
   }
 
   // ---- merge the 4 waves: M = max m_w, each wave scaled by 2^(m_w - M) ----
-  float* mbuf = reinterpret_cast<float*>(smem + 4 * VT);  // [4][32]
-  float* lbuf = mbuf + 4 * 32;                            // [4][32]
   const float l_w = l_run + xor32(l_run);
   if (hf == 0) {
     mbuf[w * 32 + r] = m_run;
     lbuf[w * 32 + r] = l_w;
   }
-  __syncthreads();  // also ends every wave's use of its V tile
+  __syncthreads();  // also ends every wave's use of its V tiles
   float M = -INFINITY;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mbuf[ww * 32 + r]);
   const float M_use = (M == -INFINITY) ? 0.0f : M;
-  const float fw = fast_exp2(m_run - M_use);
+  const float fw = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - M_use);
   // O^T fragments accumulate into obuf[d][32] (float), one wave after another
-  float* obuf = reinterpret_cast<float*>(smem);
+  float* obuf = reinterpret_cast<float*>(vs0);
   for (int ww = 0; ww < 4; ++ww) {
     if (w == ww) {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dd = 32 * d + frag_row(i, hf);
-          const float v = oacc[d][i] * fw;
+        for (int i2 = 0; i2 < 16; ++i2) {
+          const int dd = 32 * d + frag_row(i2, hf);
+          const float v = oacc[d][i2] * fw;
           obuf[dd * 32 + r] = (ww == 0) ? v : obuf[dd * 32 + r] + v;
         }
     }
@@ -259,14 +377,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
   for (int idx = tid; idx < p.G * D; idx += 256) {
     const int col = idx / D, d = idx % D;
     const int h = hkv * p.G + col;
-    // merged max and sum of this column (4 terms)
     float Mc = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) Mc = fmaxf(Mc, mbuf[ww * 32 + col]);
     const float Mcu = (Mc == -INFINITY) ? 0.0f : Mc;
     float lc = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) lc += lbuf[ww * 32 + col] * fast_exp2(mbuf[ww * 32 + col] - Mcu);
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = mbuf[ww * 32 + col];
+      lc += (mw == -INFINITY) ? 0.0f : lbuf[ww * 32 + col] * fast_exp2(mw - Mcu);
+    }
     const float o = lc > 0.0f ? obuf[d * 32 + col] / lc : 0.0f;
     if (p.num_splits == 1) {
       uint16_t* orow = p.out + ((int64_t)b * p.Hq + h) * D;
@@ -281,34 +401,71 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecParams p) {
   }
 }
 
-// One wave per (sequence, query head).
+// One wave per (sequence, query head):
+//   M = max_s LSE_s,  LSE = M + ln sum_s e^{LSE_s - M},  O = sum_s e^{LSE_s - LSE} O_s.
+// Lane s holds split s's weight (splits taken 64 at a time), broadcast by
+// shuffles; each lane accumulates output elements d = lane and lane + 64
+// with the partial loads unrolled so several are in flight.
 template <int D, int DT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecParams p) {
   const int bh = blockIdx.x;  // b * Hq + h
   const int lane = threadIdx.x;
   const int S = p.num_splits;
   const float* ls = p.ws_lse + (int64_t)bh * S;
+  const float* os = p.ws_o + (int64_t)bh * S * D;
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, ls[s]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   const float Mu = (M == -INFINITY) ? 0.0f : M;
   float sum = 0.0f;
-  for (int s = lane; s < S; s += 64) sum += __expf(ls[s] - Mu);
+  for (int s = lane; s < S; s += 64) sum += fast_exp2((ls[s] - Mu) * kLog2e);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
   const bool empty = !(sum > 0.0f);
-  const float L = empty ? INFINITY : Mu + __logf(sum);
-  for (int d = lane; d < D; d += 64) {
-    float o = 0.0f;
-    if (!empty) {
-      for (int s = 0; s < S; ++s) {
-        const float wgt = __expf(ls[s] - L);
-        o = fmaf(wgt, p.ws_o[((int64_t)bh * S + s) * D + d], o);
+  const float L = empty ? INFINITY : Mu + fast_log2(sum) * kLn2;
+  constexpr int ND = (D + 63) / 64;
+  float o[ND];
+#pragma unroll
+  for (int k = 0; k < ND; ++k) o[k] = 0.0f;
+  if (!empty) {
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int ns = min(64, S - s0);
+      const float wl = lane < ns ? fast_exp2((ls[s0 + lane] - L) * kLog2e) : 0.0f;
+      int s = 0;
+      for (; s + 8 <= ns; s += 8) {
+        float part[8][ND];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int k = 0; k < ND; ++k) {
+            const int d = lane + 64 * k;
+            part[u][k] = d < D ? os[(int64_t)(s0 + s + u) * D + d] : 0.0f;
+          }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wgt = __shfl(wl, s + u, 64);
+#pragma unroll
+          for (int k = 0; k < ND; ++k) o[k] = fmaf(wgt, part[u][k], o[k]);
+        }
+      }
+      for (; s < ns; ++s) {
+        const float wgt = __shfl(wl, s, 64);
+#pragma unroll
+        for (int k = 0; k < ND; ++k) {
+          const int d = lane + 64 * k;
+          if (d < D) o[k] = fmaf(wgt, os[(int64_t)(s0 + s) * D + d], o[k]);
+        }
       }
     }
-    const uint32_t pk = pack2<DT>(o, 0.0f);
-    p.out[(int64_t)bh * D + d] = (uint16_t)(pk & 0xffff);
+  }
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) {
+      const uint32_t pk = pack2<DT>(o[k], 0.0f);
+      p.out[(int64_t)bh * D + d] = (uint16_t)(pk & 0xffff);
+    }
   }
   if (lane == 0 && p.lse) p.lse[bh] = L;
 }

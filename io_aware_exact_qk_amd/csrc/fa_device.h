@@ -242,6 +242,11 @@ __device__ __forceinline__ void dma4(const void* src, char* lds_block) {
 // Encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt immediate that waits until at most n (< 64) vector-memory
+// operations of this wave are outstanding (vmcnt split over bits 3:0 and
+// 15:14), leaving expcnt and lgkmcnt at their maxima.
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
 // Rows [row0, row0 + ROWS) of a row-major 16-bit matrix with D columns and a
 // row stride of `rstride` elements, copied into an LDS tile laid out as
 // tile_off<D>.  The 1 KB blocks of the tile are dealt to the NWAVES waves;
