@@ -22,7 +22,10 @@ Printed as one JSON line, with
 
 Modes: ``--copy-calibration`` runs a plain device copy of known size (for
 scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters); ``--decode-only`` and
-``--fwdbwd-only`` restrict the run for profiling.
+``--fwdbwd-only`` restrict the run for profiling; ``--pmc-summary`` turns the
+counter runs into profiles/traffic.json (HBM bytes per launch per kernel,
+tagged with a hash of the kernel sources), from which ``roofline.traffic``
+is reported while the sources are unchanged.
 """
 from __future__ import annotations
 
@@ -53,6 +56,39 @@ def visible_pairs(B, H_, S, causal):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("io_aware_exact_qk_amd/csrc", "include")
+
+
+def kernel_source_hash():
+    """sha256 over every HIP/C source and header the kernels are built from,
+    so HBM traffic measured for one version is never reported for another."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in KERNEL_SOURCES:
+        base = os.path.join(ROOT, d)
+        for name in sorted(os.listdir(base)):
+            if name.endswith((".hip", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(base, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none or it was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------
@@ -130,7 +166,8 @@ def run_fwdbwd(args, torch, fa):
     dom_fl = per_pair[dom] * pairs_step * args.steps
     achieved = dom_fl / kern[dom]["total_ms"] / 1e9
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(dom),
                 "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
     return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
                 roofline=roofline, flops_step=flops_step)
@@ -192,7 +229,8 @@ def run_decode(args, torch, fa, splits=16):
             "bytes_per_call": nbytes, "best": best, "by_splits": list(res.values()),
             "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": best["split_kernel_GBps"],
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(best["split_kernel_GBps"] / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(best["split_kernel_GBps"] / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode_split")}}
 
 
 # ---------------------------------------------------------------------------
@@ -235,6 +273,65 @@ def run_copy_calibration(torch):
     print(json.dumps({"copy_bytes": n}))
 
 
+KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"), ("bwd_pre_kernel", "bwd_preprocess"),
+               ("fwd_kernel", "fwd"), ("decode_split_kernel", "decode_split"),
+               ("decode_combine_kernel", "decode_combine"))
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, dispatch id) -> value summed over the counter's instances,
+    from a rocprofv3 --pmc --output-format csv directory."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench,
+    then of the 1 GiB copy calibration) into profiles/traffic.json: HBM bytes
+    per launch of each kernel, each counter scaled so that the plain copy reads
+    and writes exactly 1 GiB."""
+    import statistics
+
+    def per_kernel(rows):
+        acc = {}
+        for (name, _), v in rows.items():
+            for pat, key in KERNEL_KEYS:
+                if pat in name:
+                    acc.setdefault(key, []).append(v)
+        return {k: statistics.mean(v) for k, v in acc.items()}
+
+    def copy_kib(rows):
+        vals = [v for (name, _), v in rows.items() if "copy" in name.lower()]
+        return statistics.median(vals) if vals else None
+
+    f_cal, w_cal = copy_kib(_pmc_rows(cal_fetch_dir, "FETCH_SIZE")), copy_kib(_pmc_rows(cal_write_dir, "WRITE_SIZE"))
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / f_cal if f_cal else 1.0
+    w_scale = gib_kib / w_cal if w_cal else 1.0
+    fk, wk = per_kernel(_pmc_rows(fetch_dir, "FETCH_SIZE")), per_kernel(_pmc_rows(write_dir, "WRITE_SIZE"))
+    kernels = {}
+    for key in sorted(set(fk) | set(wk)):
+        fb, wb = fk.get(key, 0.0) * 1024 * f_scale, wk.get(key, 0.0) * 1024 * w_scale
+        kernels[key] = {"fetch_kib_raw": round(fk.get(key, 0.0), 1), "write_kib_raw": round(wk.get(key, 0.0), 1),
+                        "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    rec = {"source_sha256": kernel_source_hash(), "copy_calibration": {
+        "copy_bytes": 1 << 30, "fetch_kib": f_cal, "write_kib": w_cal, "fetch_scale": f_scale, "write_scale": w_scale},
+        "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +341,12 @@ def main():
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--fwdbwd-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write profiles/traffic.json from four rocprofv3 --pmc output directories")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
