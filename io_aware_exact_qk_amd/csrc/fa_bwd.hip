@@ -23,6 +23,8 @@
 //      accumulates dQ^T += K^T dS^T.
 // Both recompute kernels fit in 256 VGPRs, so two waves share each SIMD and
 // one wave's exponentials overlap the other's matrix instructions.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_host.h"
 
@@ -394,7 +396,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       const int j0 = t * BC;
       // keys past the end hold a copy of the last key: classify marks such tiles partial
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
-      if (cls != 0) {
+      // The tile body is written out twice, without and with the mask, so the
+      // common unmasked case is one basic block in which the scheduler can
+      // overlap one 32-key half's exponentials with the other half's MFMAs:
+      // S/dP(0), S/dP(1), P/dS(0), dQ(0), P/dS(1), dQ(1).
+      auto body = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -406,47 +413,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
             dp[kb] = mfma32<DT>(lds_nat(vt + (kb * 32) * (D * 2), nbv, c), doreg[c], dp[kb]);
           }
         }
-        // logits, mask (keys past Sk hold a copy of the last key), P and dS
-        if constexpr (SOFTCAP || ALIBI) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = j0 + 32 * kb + frag_row(i, g);
-              s[kb][i] = logit2<SOFTCAP, ALIBI>(s[kb][i], ip, j, p, slope_log2);
-            }
-        }
-        if (cls == 1) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = j0 + 32 * kb + frag_row(i, g);
-              s[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? s[kb][i] : -INFINITY;
-            }
-        }
+        // all S/dP MFMAs are issued before any exponential: the matrix core
+        // works through the second half while the VALU handles the first
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          // logits, mask (keys past Sk hold a copy of the last key), P and dS
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float pv = fast_exp2(fmaf(s[kb][i], fs, -lse2));
+            const int j = j0 + 32 * kb + frag_row(i, g);
+            float x = s[kb][i];
+            if constexpr (SOFTCAP || ALIBI) x = logit2<SOFTCAP, ALIBI>(x, ip, j, p, slope_log2);
+            if constexpr (MASKED) x = (row_ok & visible(ip, j, Sk, mask)) ? x : -INFINITY;
+            const float pv = fast_exp2(fmaf(x, fs, -lse2));
             float ds = pv * (dp[kb][i] - dv_row);
-            if constexpr (SOFTCAP) {
-              ds = softcap_grad<ALIBI>(ds, pv, s[kb][i], ip, j0 + 32 * kb + frag_row(i, g), p, slope_log2);
-            }
+            if constexpr (SOFTCAP) ds = softcap_grad<ALIBI>(ds, pv, x, ip, j, p, slope_log2);
             dp[kb][i] = ds;
           }
-        }
-        // dQ^T += K^T dS^T  (contraction over the 64 keys)
+          // dQ^T += K^T dS^T over this half's 32 keys
 #pragma unroll
-        for (int mk = 0; mk < 4; ++mk) {
-          const u32x4 db = pack_frag_half<DT>(dp[mk >> 1], mk & 1);
+          for (int mh = 0; mh < 2; ++mh) {
+            const int mk = 2 * kb + mh;
+            const u32x4 db = pack_frag_half<DT>(dp[kb], mh);
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            dqacc[d] = mfma32<DT>(lds_At<D>(kt + (16 * mk) * (D * 2), tbv, d), db, dqacc[d]);
+            for (int d = 0; d < DB; ++d) {
+              dqacc[d] = mfma32<DT>(lds_At<D>(kt + (16 * mk) * (D * 2), tbv, d), db, dqacc[d]);
+            }
           }
         }
-      }
+      };
+      if (cls == 2) body(std::false_type{});
+      else if (cls == 1) body(std::true_type{});
       dma_wait();
       __syncthreads();
     };
