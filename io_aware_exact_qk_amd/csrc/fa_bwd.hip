@@ -158,7 +158,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int g = lane >> 5, r = lane & 31;
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
@@ -385,8 +386,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
     auto issue = [&](int t, char* kt) {
-      dma_tile<D, BC, 4>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
-      dma_tile<D, BC, 4>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4, false>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4, false>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
     // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
     auto step = [&](const char* kt, char* nxt, int t) {

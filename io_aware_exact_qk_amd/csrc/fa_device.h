@@ -249,23 +249,40 @@ constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 
 // Rows [row0, row0 + ROWS) of a row-major 16-bit matrix with D columns and a
 // row stride of `rstride` elements, copied into an LDS tile laid out as
-// tile_off<D>.  The 1 KB blocks of the tile are dealt to the NWAVES waves;
-// lane l of a block writes physical chunk l % (D/8) of its row, so it loads
-// the logical chunk that the swizzle maps there.  Rows at or past `nrows`
-// (>= 1) re-read row nrows - 1 (valid memory); callers mask those rows.
-template <int D, int ROWS, int NWAVES>
+// tile_off<D>.  The 1 KB blocks of the tile are dealt to the NWAVES waves
+// (w must be wave-uniform); lane l of a block writes physical chunk
+// l % (D/8) of its row, so it loads the logical chunk that the swizzle maps
+// there.  When every row is in range the source address is a wave-uniform
+// base (scalar arithmetic) plus a 32-bit lane offset that does not change
+// between tiles; otherwise rows at or past `nrows` (>= 1) re-read row
+// nrows - 1 (valid memory) and callers mask those rows.  FAST = false always
+// takes the clamped form (fewer live values, for kernels at the VGPR limit).
+template <int D, int ROWS, int NWAVES, bool FAST = true>
 __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64_t rstride, int row0,
                                          int nrows, int w, int lane) {
   constexpr int NCH = D / 8, RPB = 64 / NCH, NBLK = ROWS / RPB;
   static_assert(NBLK % NWAVES == 0, "tile blocks must divide among the waves");
   const int rin = lane / NCH, pch = lane % NCH;
+  if (FAST && row0 + ROWS <= nrows) {
+    const char* b0 = reinterpret_cast<const char*>(base + (int64_t)row0 * rstride);
 #pragma unroll
-  for (int i = 0; i < NBLK / NWAVES; ++i) {
-    const int blk = i * NWAVES + w;
-    const int row = blk * RPB + rin;
-    const int lch = pch ^ (int)swz<D>(row);
-    const int grow = min(row0 + row, nrows - 1);
-    dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+    for (int i = 0; i < NBLK / NWAVES; ++i) {
+      const int blk = i * NWAVES + w;
+      const int row = blk * RPB + rin;
+      // re-derived per call: hoisting whole 64-bit addresses out of the tile
+      // loop would cost two VGPRs per block
+      const uint32_t loff = opaque((uint32_t)(rin * rstride + ((pch ^ (int)swz<D>(row)) << 3)) * 2u);
+      dma16(b0 + (int64_t)blk * RPB * rstride * 2 + loff, tile + blk * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBLK / NWAVES; ++i) {
+      const int blk = i * NWAVES + w;
+      const int row = blk * RPB + rin;
+      const int lch = pch ^ (int)swz<D>(row);
+      const int grow = min(row0 + row, nrows - 1);
+      dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+    }
   }
 }
 

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char vb0[TILE];
   __shared__ __attribute__((aligned(1024))) char vb1[TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int g = lane >> 5, r = lane & 31;
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
@@ -214,6 +215,57 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       }
     };
 
+    // The pipelined block in an explicit instruction order.  S of the next
+    // tile: a ring of four K fragments keeps four LDS reads in flight ahead of
+    // the MFMA that consumes them, and each MFMA is followed by a slice of the
+    // current tile's softmax (exponentials, row sum, packing of P).  Then
+    // O += P V with a ring of three V^T fragments (six transposed reads) in
+    // flight.  sched_barrier fences keep the scheduler from pulling each read
+    // down next to its MFMA, which would expose the whole LDS latency on
+    // every MFMA.
+    auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, f32x16 (&sc)[2],
+                     f32x16 (&sn)[2], float m_use) {
+      constexpr int NS = 2 * KC;    // S MFMAs per tile
+      constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
+      u32x4 kr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = lds_nat(kn + (i / KC) * 32 * (D * 2), nbv, i % KC);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      float lsum = 0.0f;
+      u32x4 pb[4];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int kb = i / KC, c = i % KC;
+        sn[kb] = mfma32<DT>(kr[i & 3], qreg[c], sn[kb]);
+        if (i + 4 < NS) kr[i & 3] = lds_nat(kn + ((i + 4) / KC) * 32 * (D * 2), nbv, (i + 4) % KC);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int idx = i * EPS + e;
+          const float pv = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
+          sc[idx >> 4][idx & 15] = pv;
+          lsum += pv;
+        }
+        if (((i + 1) * EPS) % 8 == 0) {
+          const int mk = (i + 1) * EPS / 8 - 1;
+          pb[mk] = pack_frag_half<DT>(sc[mk >> 1], mk & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run += lsum;
+      constexpr int NP = 4 * DB;  // P V MFMAs per tile
+      u32x4 vr[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) vr[i] = lds_At<D>(vt + (16 * (i / DB)) * (D * 2), tbv, i % DB);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int mk = i / DB, d = i % DB;
+        oacc[d] = mfma32<DT>(vr[i % 3], pb[mk], oacc[d]);
+        if (i + 3 < NP) vr[i % 3] = lds_At<D>(vt + (16 * ((i + 3) / DB)) * (D * 2), tbv, (i + 3) % DB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
     // Pipelined step for tile t (t + 1 < t_hi): `sc` holds S of tile t, the
     // MFMAs of S for tile t + 1 (K in `kn`, into `sn`) run in the same basic
     // block as the exponentials of tile t, then O += P V with V of tile t in
@@ -225,10 +277,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       dma_v(t + 1, vdst);
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const float m_use = prep(t, sc);
-      u32x4 pb[4];
-      qk(kn, nbv, sn);
-      expo(sc, m_use, pb);
-      pv(vt, tbv, pb);
+      fused(kn, vt, nbv, tbv, sc, sn, m_use);
       dma_wait();
       __syncthreads();
     };
