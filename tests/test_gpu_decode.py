@@ -110,3 +110,40 @@ def test_cfg5_full(num_splits):
     assert_out(out, ref["out"], torch.bfloat16)
     assert_lse(lse, ref["lse"])
     _check_cache(c, ref, kc, vc)
+
+
+# Rotary half-widths of 8 and 24 elements (rotary_dim 16 and 48): the partner
+# of a chunk then sits in the other half of the wave's chunk split.
+@pytest.mark.parametrize("rotary_dim", [16, 48])
+def test_partial_rotary_odd_chunk_offset(rotary_dim):
+    c = decode_case(B=3, Hq=8, Hkv=2, D=128, page=64, seqlens=[190, 64, 1], seed=54, rotary_dim=rotary_dim)
+    say("decode rotary_dim", rotary_dim)
+    out, lse, kc, vc = _run(c, 3)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)
+
+
+def test_large_batch_unsorted_order():
+    """More sequences than the longest-first scheduler ranks (identity order)."""
+    lens = [int(x) for x in np.random.default_rng(55).integers(0, 300, size=70)]
+    c = decode_case(B=70, Hq=4, Hkv=2, D=64, page=32, seqlens=lens, seed=55)
+    say("decode B=70")
+    out, lse, kc, vc = _run(c, 2)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)
+
+
+def test_many_splits_combine():
+    """More splits than one wave's lanes (the combine walks them 64 at a time),
+    most of them empty."""
+    c = decode_case(B=2, Hq=8, Hkv=2, D=128, page=32, seqlens=[4000, 33], seed=56)
+    say("decode 100 splits")
+    out, lse, kc, vc = _run(c, 100)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)

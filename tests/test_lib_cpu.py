@@ -43,8 +43,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.fa_bwd_workspace_size(2, 512, 512, 16, 16, 128, 0) == 2 * 16 * 512 * 4
-    assert lib.fa_bwd_varlen_workspace_size(1000, 3, 128, 0) == 12032  # 12000 rounded up to 256
+    # two float32 row arrays (row term, LSE in log2 units), each padded to 256 bytes
+    assert lib.fa_bwd_workspace_size(2, 512, 512, 16, 16, 128, 0) == 2 * (2 * 16 * 512 * 4)
+    assert lib.fa_bwd_varlen_workspace_size(1000, 3, 128, 0) == 2 * 12032  # 12000 rounded up to 256
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 1) == 0
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 16) == 8 * 32 * 16 * 128 * 4 + 8 * 32 * 16 * 4
 
