@@ -49,7 +49,7 @@ struct BwdParams {
   float scale, scale_log2, scale_over_cap, cap_log2, inv_cap_log2;
   const float* alibi;
   int wl, wr;
-  int n_tiles, n_heads, n_batch, reverse;
+  int n_tiles, n_heads, n_batch, reverse, balanced;
   int n_tokens;  // preprocess: number of (token) rows
 };
 
@@ -163,11 +163,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int g = lane >> 5, r = lane & 31;
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
-  const int nwg = p.n_tiles * p.n_heads * p.n_batch;
-  const int id = xcd_remap((int)blockIdx.x, nwg);
-  const int tk = id % p.n_tiles;
-  const int hk = (id / p.n_tiles) % p.n_heads;
-  const int b = id / (p.n_tiles * p.n_heads);
+  // causal: the first key tiles are seen by the most queries
+  const TileId tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, false);
+  const int tk = tid3.t, hk = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
   const int k0 = tk * BC;
   if (k0 >= sb.Sk) return;
@@ -337,12 +335,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int g = lane >> 5, r = lane & 31;
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
-  const int nwg = p.n_tiles * p.n_heads * p.n_batch;
-  const int id = xcd_remap((int)blockIdx.x, nwg);
-  int tq = id % p.n_tiles;
-  const int h = (id / p.n_tiles) % p.n_heads;
-  const int b = id / (p.n_tiles * p.n_heads);
-  if (p.reverse) tq = p.n_tiles - 1 - tq;
+  // causal: the last query tiles see the most keys
+  const TileId tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, p.reverse != 0);
+  const int tq = tid3.t, h = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
   const int q0 = tq * BR;
   if (q0 >= sb.Sq) return;
@@ -519,11 +514,13 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   kv.n_heads = Hkv;
   kv.n_batch = nbatch;
   kv.reverse = 0;
+  kv.balanced = causal ? 1 : 0;
   BwdParams dq = base;
   dq.n_tiles = (max_sq + 127) / 128;
   dq.n_heads = base.Hq;
   dq.n_batch = nbatch;
   dq.reverse = causal ? 1 : 0;
+  dq.balanced = causal ? 1 : 0;
   const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * nbatch;
   const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * nbatch;
   if (nwg_pre > 0x7fffffffLL || nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;

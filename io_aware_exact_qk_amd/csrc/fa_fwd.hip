@@ -67,12 +67,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint32_t tb = tr_base<D>(lane);
 
   // logical tile id -> (q tile, head, batch)
-  const int nwg = p.n_qtiles * p.n_heads * p.n_batch;
-  const int id = xcd_remap((int)blockIdx.x, nwg);
-  int tq = id % p.n_qtiles;
-  const int h = (id / p.n_qtiles) % p.n_heads;
-  const int b = id / (p.n_qtiles * p.n_heads);
-  if (p.reverse) tq = p.n_qtiles - 1 - tq;
+  // causal: the last query tiles see the most keys
+  const TileId tid3 = tile_id(p.n_qtiles, p.n_heads, p.n_batch, p.reverse != 0, p.reverse != 0);
+  const int tq = tid3.t, h = tid3.h, b = tid3.b;
 
   int q_start, Sq, k_start, Sk;
   if (p.cu_q) {

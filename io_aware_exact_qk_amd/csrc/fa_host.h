@@ -29,13 +29,39 @@ inline int check_common(int Hq, int Hkv, int D, int dtype, float scale, int wl, 
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Work-group ids are handed to the 8 XCDs round-robin (id % 8).  The kernels
-// remap the hardware id so that each XCD receives one contiguous block of
-// logical tiles, which keeps tiles that share K/V rows on the same L2.
-__device__ __forceinline__ int xcd_remap(int hw_id, int n) {
-  const int per = n / 8;
-  if (hw_id >= per * 8) return hw_id;
-  return (hw_id & 7) * per + (hw_id >> 3);
+// Work-group ids are handed to the 8 XCDs round-robin (id % 8).
+struct TileId {
+  int t, h, b;  // tile index along the sequence, head, batch entry
+};
+
+// Logical coordinates of this work-group.
+//  * default: the hardware id is remapped so that each XCD receives one
+//    contiguous block of logical tiles, which keeps tiles that share K/V (or
+//    Q/dO) rows on the same L2;
+//  * balanced (causal launches, where tiles differ a lot in work): ids are
+//    taken tile-major in hardware order, so the heaviest tile of every
+//    (head, batch) is dispatched first and neighbouring tiles go to
+//    different XCDs.  heavy_last: the heaviest tile is the last one.
+__device__ __forceinline__ TileId tile_id(int n_tiles, int n_heads, int n_batch, bool balanced,
+                                          bool heavy_last) {
+  TileId r;
+  const int hw = (int)blockIdx.x;
+  int t;
+  if (balanced) {
+    const int hb = hw % (n_heads * n_batch);
+    t = hw / (n_heads * n_batch);
+    r.h = hb % n_heads;
+    r.b = hb / n_heads;
+  } else {
+    const int n = n_tiles * n_heads * n_batch;
+    const int per = n / 8;
+    const int id = (hw >= per * 8) ? hw : (hw & 7) * per + (hw >> 3);
+    t = id % n_tiles;
+    r.h = (id / n_tiles) % n_heads;
+    r.b = id / (n_tiles * n_heads);
+  }
+  r.t = heavy_last ? n_tiles - 1 - t : t;
+  return r;
 }
 
 // ---- kernel timing (implemented in fa_api.hip) ----
