@@ -195,7 +195,8 @@ def run_decode(args, torch, fa, splits=16):
     out = torch.empty_like(q)
     lse = torch.empty(8, 32, 1, device=dev, dtype=torch.float32)
     res = {}
-    for ns in sorted(set([1, 4, splits])):
+    # 0 = the library's automatic choice
+    for ns in [1, 4, splits, 0] if splits not in (1, 4, 0) else [1, 4, 0]:
         ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
                          dtype=torch.uint8)
 

@@ -151,11 +151,18 @@ size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministi
  *   out (B, Sq_new, Hq, D) out; lse (B, Hq, Sq_new) float32 out or NULL.
  *   num_splits >= 1: the keys of each sequence are cut into num_splits
  *     contiguous page ranges processed in parallel and merged exactly; the
- *     result does not depend on it beyond float32 rounding.
- *   causal: accepted; with Sq_new == 1 the new query sees every key.
- *   window_left/right, softcap, alibi_slopes: must be -1/-1, 0 and NULL in
- *     this build (FA_ERR_UNSUPPORTED otherwise).
- *   workspace: fa_kvcache_workspace_size(...) bytes (0 when num_splits == 1).
+ *     result does not depend on it beyond float32 rounding.  num_splits == 0:
+ *     the library chooses (about 1024 work-groups over B * Hkv, at most 32
+ *     splits and at most max_blocks_per_seq).
+ *   causal: accepted; with Sq_new == 1 the new query sits at the last
+ *     position (bottom-right alignment) and sees every earlier key.
+ *   window_left (-1 = unbounded): keys before position
+ *     cache_seqlens[b] + Sq_new - 1 - window_left are masked; window_right
+ *     has no effect with Sq_new == 1.
+ *   softcap (0 = off) and alibi_slopes (NULL or float32 (Hq,)): as in
+ *     fa_fwd, with the ALiBi distance measured from the new query's position.
+ *   workspace: fa_kvcache_workspace_size(...) bytes (0 when num_splits == 1),
+ *     computed with the same num_splits argument (0 included).
  * Appended slot (b, cache_seqlens[b] + t) receives the rotated k_new rounded
  * once to the cache dtype and v_new unchanged; no other cache byte changes.
  */
@@ -170,7 +177,8 @@ int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_new,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace for fa_fwd_kvcache: float32 split partials O_s (B,Hq,Sq_new,num_splits,D)
- * and LSE_s (B,Hq,Sq_new,num_splits), or 0 when num_splits == 1. */
+ * and LSE_s (B,Hq,Sq_new,num_splits), or 0 when num_splits == 1; num_splits == 0
+ * returns the size for 32 splits, enough for any automatic choice. */
 size_t fa_kvcache_workspace_size(int B, int Sq_new, int Hq, int D, int num_splits);
 
 /*

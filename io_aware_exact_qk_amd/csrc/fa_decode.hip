@@ -32,6 +32,8 @@
 // split the kernel writes the final output; otherwise it writes float32
 // partials (O_s normalised, LSE_s) that the combine kernel merges with
 //   M = max_s LSE_s,  LSE = M + ln sum_s e^{LSE_s - M},  O = sum_s e^{LSE_s - LSE} O_s.
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_host.h"
 
@@ -55,6 +57,12 @@ struct DecParams {
   float* ws_lse;
   int B, Hq, Hkv, G, num_splits;
   float scale_log2;
+  // logit options (the OPTS kernels): softcap c (cap_log2 = c log2 e,
+  // scale_over_cap = scale / c; 0 = off), ALiBi slopes per query head, and a
+  // left window (-1 = unbounded)
+  float cap_log2, scale_over_cap;
+  const float* alibi;
+  int wl;
 };
 
 template <int DT>
@@ -75,7 +83,10 @@ typedef __attribute__((address_space(4))) const int cint;  // constant address s
 // Batches up to this size are scheduled longest cache first.
 constexpr int kDecodeSortMax = 64;
 
-template <int D, int DT>
+// OPTS: softcap, ALiBi or a left window is on.  The new query sits at
+// position n_keys - 1 (bottom-right alignment), sees every key at or before
+// it, and with a left window w only keys >= n_keys - 1 - w.
+template <int D, int DT, bool OPTS>
 __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int BK = 32;  // keys per wave tile
   constexpr int KC = D / 16, DB = D / 32;
@@ -129,10 +140,13 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   const int n_keys = L + (append ? 1 : 0);
   const int page = p.page_size;
   const int n_pages = (n_keys + page - 1) / page;
-  const int per = (n_pages + p.num_splits - 1) / p.num_splits;
-  const int p_lo = s_id * per;
+  // first visible key; the splits share the pages from its page on
+  const int key_lo = (OPTS && p.wl >= 0) ? max(0, n_keys - 1 - p.wl) : 0;
+  const int pg0 = key_lo / page;
+  const int per = (n_pages - pg0 + p.num_splits - 1) / p.num_splits;
+  const int p_lo = pg0 + s_id * per;
   const int p_hi = min(n_pages, p_lo + per);
-  const int k_lo = p_lo * page;
+  const int k_lo = max(p_lo * page, key_lo);
   const int k_hi = min(p_hi * page, n_keys);
 
   // ---- stage the group's query rows, the k_new row and the rotary row of
@@ -207,6 +221,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  const float slope_log2 = (OPTS && p.alibi && col_ok) ? p.alibi[hkv * p.G + r] * kLog2e : 0.0f;
 
   // Element offset of the first row of the 32-key tile starting at key j0
   // (a tile never crosses a page: page_size is a multiple of 32).  Rows of
@@ -260,14 +275,27 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
       sl = mfma32<DT>(ka[c], qlo[c], sl);
     }
     s += sl;
-    if (j0 + BK > n_keys) {
+    if constexpr (OPTS) {
+      // final logits in log2 units: softcap, then the ALiBi distance term
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = (j0 + frag_row(i, hf) < n_keys) ? s[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        float x = p.cap_log2 > 0.0f ? p.cap_log2 * tanh_exp(s[i] * p.scale_over_cap) : s[i] * p.scale_log2;
+        if (p.alibi) x -= slope_log2 * (float)(n_keys - 1 - (j0 + frag_row(i, hf)));
+        s[i] = x;
+      }
+    }
+    if (j0 + BK > n_keys || (OPTS && j0 < key_lo)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + frag_row(i, hf);
+        s[i] = (j < n_keys && j >= key_lo) ? s[i] : -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;
+    mx = fmaxf(mx, xor32(mx));
+    if constexpr (!OPTS) mx *= p.scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
@@ -280,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     float lsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pv = fast_exp2(fmaf(s[i], p.scale_log2, -m_use));
+      const float pv = fast_exp2(fmaf(s[i], OPTS ? 1.0f : p.scale_log2, -m_use));
       s[i] = pv;
       lsum += pv;
     }
@@ -471,11 +499,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecParams p) {
 }
 
 template <int D, int DT>
-static int launch_decode(const DecParams& p, hipStream_t st) {
+static int launch_decode(const DecParams& p, bool opts, hipStream_t st) {
   const long long nwg = (long long)p.B * p.Hkv * p.num_splits;
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   prof_before(FA_KERNEL_DECODE_SPLIT, st);
-  hipLaunchKernelGGL((decode_split_kernel<D, DT>), dim3((int)nwg), dim3(256), 0, st, p);
+  if (opts) hipLaunchKernelGGL((decode_split_kernel<D, DT, true>), dim3((int)nwg), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((decode_split_kernel<D, DT, false>), dim3((int)nwg), dim3(256), 0, st, p);
   prof_after(FA_KERNEL_DECODE_SPLIT, st);
   if (p.num_splits > 1) {
     prof_before(FA_KERNEL_DECODE_COMBINE, st);
@@ -485,11 +514,27 @@ static int launch_decode(const DecParams& p, hipStream_t st) {
   return launch_status();
 }
 
+// num_splits = 0 lets the library choose.  The split kernel holds one
+// work-group per CU (256 CUs), and an HBM-bound stream wants several rounds
+// of them in flight, so the choice aims at about 1024 work-groups, with at
+// most kAutoSplitMax splits and no more splits than pages.
+constexpr int kAutoSplitMax = 32;
+constexpr int kAutoTargetGroups = 1024;
+
+static int auto_splits(int B, int Hkv, int max_pages) {
+  const long long groups = (long long)B * Hkv;
+  long long s = (kAutoTargetGroups + groups - 1) / groups;
+  s = std::min<long long>(s, kAutoSplitMax);
+  s = std::min<long long>(s, max_pages);
+  return (int)std::max<long long>(s, 1);
+}
+
 }  // namespace fa
 
 using namespace fa;
 
 extern "C" size_t fa_kvcache_workspace_size(int B, int Sq_new, int Hq, int D, int num_splits) {
+  if (num_splits == 0) num_splits = kAutoSplitMax;  // enough for any automatic choice
   if (B < 1 || Sq_new < 1 || Hq < 1 || D < 1 || num_splits <= 1) return 0;
   const size_t parts = (size_t)B * Sq_new * Hq * num_splits;
   return align_up(parts * D * sizeof(float), 256) + align_up(parts * sizeof(float), 256);
@@ -507,7 +552,7 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   (void)causal;
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
-  if (B < 1 || Sq_new < 1 || num_splits < 1 || max_blocks_per_seq < 1) return FA_ERR_INVALID_ARG;
+  if (B < 1 || Sq_new < 1 || num_splits < 0 || max_blocks_per_seq < 1) return FA_ERR_INVALID_ARG;
   if (page_size < 32 || page_size % 32 != 0) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return FA_ERR_INVALID_ARG;
   if (!aligned4(cache_seqlens)) return FA_ERR_INVALID_ARG;
@@ -518,9 +563,10 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   if ((rotary_cos == nullptr) != (rotary_sin == nullptr)) return FA_ERR_INVALID_ARG;
   if (rotary_cos && (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > D)) return FA_ERR_INVALID_ARG;
   if (rotary_cos && (!aligned4(rotary_cos) || !aligned4(rotary_sin))) return FA_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
   if (Sq_new != 1) return FA_ERR_UNSUPPORTED;
-  if (window_left != -1 || window_right != -1 || softcap != 0.0f || alibi_slopes) return FA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  if (num_splits == 0) num_splits = auto_splits(B, Hkv, max_blocks_per_seq);
   const size_t need = fa_kvcache_workspace_size(B, Sq_new, Hq, D, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
 
@@ -548,9 +594,16 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   p.G = Hq / Hkv;
   p.num_splits = num_splits;
   p.scale_log2 = scale * kLog2e;
+  p.cap_log2 = softcap * kLog2e;
+  p.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
+  p.alibi = alibi_slopes;
+  p.wl = window_left;
+  // one new query at the last position sees every earlier key, so only a
+  // left window, softcap or ALiBi changes the scores
+  const bool opts = softcap > 0.0f || alibi_slopes != nullptr || window_left >= 0;
   hipStream_t s = (hipStream_t)stream;
   if (D == 128) {
-    return dtype == FA_DTYPE_BF16 ? launch_decode<128, DT_BF16>(p, s) : launch_decode<128, DT_F16>(p, s);
+    return dtype == FA_DTYPE_BF16 ? launch_decode<128, DT_BF16>(p, opts, s) : launch_decode<128, DT_F16>(p, opts, s);
   }
-  return dtype == FA_DTYPE_BF16 ? launch_decode<64, DT_BF16>(p, s) : launch_decode<64, DT_F16>(p, s);
+  return dtype == FA_DTYPE_BF16 ? launch_decode<64, DT_BF16>(p, opts, s) : launch_decode<64, DT_F16>(p, opts, s);
 }

@@ -5,13 +5,13 @@ import torch
 
 import io_aware_exact_qk_amd as fa
 from oracle import kvcache_fwd
-from workloads import decode_case, cfg5
+from workloads import decode_case, cfg5, alibi_slopes
 from _helpers import DEV, assert_out, assert_lse, say, np64
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(c, num_splits, append=True, block_table="given"):
+def _run(c, num_splits, append=True, block_table="given", **opts):
     q = c.q.to(DEV)
     kc, vc = c.k_cache.to(DEV), c.v_cache.to(DEV)
     bt = c.block_table.to(DEV) if (c.block_table is not None and block_table == "given") else None
@@ -20,15 +20,16 @@ def _run(c, num_splits, append=True, block_table="given"):
                                  c.k_new.to(DEV) if append else None,
                                  c.v_new.to(DEV) if append else None,
                                  bt, rot[0], rot[1], c.rotary_dim if rot[0] is not None else None,
-                                 num_splits=num_splits, scale=c.scale)
+                                 num_splits=num_splits, scale=c.scale, **opts)
     torch.cuda.synchronize()
     return out, lse, kc, vc
 
 
-def _oracle(c, append=True):
+def _oracle(c, append=True, **opts):
     return kvcache_fwd(c.q, c.k_new if append else None, c.v_new if append else None, c.k_cache,
                        c.v_cache, c.cache_seqlens, c.block_table, c.page_size, c.rotary_cos,
-                       c.rotary_sin, c.rotary_dim, c.scale, cache_dtype="bf16" if c.q.dtype == torch.bfloat16 else "fp16")
+                       c.rotary_sin, c.rotary_dim, c.scale,
+                       cache_dtype="bf16" if c.q.dtype == torch.bfloat16 else "fp16", **opts)
 
 
 def _check_cache(c, ref, kc, vc, paged=True):
@@ -143,6 +144,50 @@ def test_many_splits_combine():
     c = decode_case(B=2, Hq=8, Hkv=2, D=128, page=32, seqlens=[4000, 33], seed=56)
     say("decode 100 splits")
     out, lse, kc, vc = _run(c, 100)
+    ref = _oracle(c)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)
+
+
+# Logit options: softcap, ALiBi and a left window.  The window edge falls
+# inside a page, on a page boundary, past the start of the cache, and at 0
+# (the new query sees only itself).
+OPTS = [
+    # window_left, softcap, alibi
+    (100, 0.0, False),
+    (64, 0.0, False),
+    (0, 0.0, False),
+    (5000, 0.0, False),
+    (-1, 30.0, False),
+    (-1, 0.0, True),
+    (150, 20.0, True),
+]
+
+
+@pytest.mark.parametrize("opt", OPTS, ids=[f"o{i}" for i in range(len(OPTS))])
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_decode_logit_options(opt, num_splits):
+    wl, sc, al = opt
+    c = decode_case(B=3, Hq=8, Hkv=2, D=128, page=64, seqlens=[700, 63, 200], seed=57, rotary_dim=64)
+    slopes = alibi_slopes(8) if al else None
+    say("decode options", opt, num_splits)
+    out, lse, kc, vc = _run(c, num_splits, window=(wl, -1), softcap=sc,
+                            alibi_slopes=None if slopes is None else slopes.to(DEV))
+    ref = _oracle(c, window=(wl, -1), softcap=sc, alibi_slopes=slopes)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)
+
+
+@pytest.mark.parametrize("B,Hkv,lens", [(1, 8, [5000]), (8, 8, None), (40, 2, None)])
+def test_auto_splits(B, Hkv, lens):
+    """num_splits = 0: the library picks the count; the result is the oracle's."""
+    if lens is None:
+        lens = [int(x) for x in np.random.default_rng(58).integers(1, 3000, size=B)]
+    c = decode_case(B=B, Hq=4 * Hkv, Hkv=Hkv, D=128, page=256, seqlens=lens, seed=58)
+    say("decode auto splits", B, Hkv)
+    out, lse, kc, vc = _run(c, 0)
     ref = _oracle(c)
     assert_out(out, ref["out"], c.q.dtype)
     assert_lse(lse, ref["lse"])

@@ -48,6 +48,8 @@ def test_workspace_sizes(lib):
     assert lib.fa_bwd_varlen_workspace_size(1000, 3, 128, 0) == 2 * 12032  # 12000 rounded up to 256
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 1) == 0
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 16) == 8 * 32 * 16 * 128 * 4 + 8 * 32 * 16 * 4
+    # num_splits = 0 (automatic) is sized for the largest automatic choice, 32
+    assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 0) == 8 * 32 * 32 * 128 * 4 + 8 * 32 * 32 * 4
 
 
 # Fake, 16-byte aligned "device" addresses: the calls below must fail in
@@ -97,12 +99,12 @@ def test_kvcache_rejects(lib):
     assert call(cos=F, sin=F, rd=24) == 1
     assert call(cos=F, sin=F, rd=256) == 1
     assert call(knew=None) == 1
-    assert call(splits=0) == 1
+    assert call(splits=-1) == 1
     assert call(Sq=2) == 2
-    assert call(wl=5) == 2
-    assert call(softcap=3.0) == 2
     assert call(Hq=66, Hkv=1) == 2
     assert call(splits=4) == 3  # needs a workspace
+    assert call(splits=0) == 3  # the automatic count here is 4: needs a workspace
+    assert call(splits=4, wl=5, softcap=3.0) == 3
 
 
 def test_varlen_rejects(lib):
