@@ -19,6 +19,7 @@ Modules
 attention : dense forward / backward (GQA, causal, window, softcap, ALiBi)
 varlen    : packed variable-length forward / backward (per-sequence slices)
 kvcache   : rotary embedding, paged-cache append and decode attention
+dropout   : Philox4x32-10 and the attention-dropout keep mask
 
 Every function is pinned by CPU tests (``tests/test_oracle_*.py``) against
 library routines, closed forms, invariants, brute force and finite
@@ -27,3 +28,4 @@ differences; none of it is "parity unpinned".
 from .attention import attention_fwd, attention_bwd, allowed_mask, score_transform  # noqa: F401
 from .varlen import varlen_fwd, varlen_bwd  # noqa: F401
 from .kvcache import rotary_apply, round_bf16, kvcache_fwd, gather_logical_cache  # noqa: F401
+from .dropout import philox4, keep_mask, keep_scale, threshold  # noqa: F401

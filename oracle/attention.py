@@ -33,6 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .dropout import keep_mask, keep_scale
+
 ROW_CHUNK = 1024  # query rows materialised at once (full rows, no tiling of keys)
 
 
@@ -105,14 +107,26 @@ def _softmax_rows(z, ok):
     return P, lse
 
 
+def _dropped(P, dropout, bh, rows, cols):
+    """(P * K * scale, K * scale) for dropout = (p, seed, offset), else (P, None)."""
+    if dropout is None:
+        return P, None
+    p, seed, offset = dropout
+    km = keep_mask(p, seed, offset, bh, rows, cols) * keep_scale(p)
+    return P * km, km
+
+
 def attention_fwd(q, k, v, scale, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, heads=None, q_rows=None):
+                  alibi_slopes=None, heads=None, q_rows=None, dropout=None, batch0=0):
     """Standard attention forward in float64.
 
     q (B, Sq, Hq, D); k, v (B, Sk, Hkv, D) — any float dtype, converted exactly.
     Returns (out, lse): out (B, Sq, Hq, D) float64, lse (B, Hq, Sq) float64.
     ``heads`` / ``q_rows`` restrict the work to a subset (other entries are
     NaN) so that single rows of very long sequences can be checked.
+    ``dropout`` = (p, seed, offset) drops attention weights as defined in
+    ``oracle.dropout`` (batch entry b counts as b + batch0); LSE is that of
+    the undropped weights.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Sq, Hq, D = q.shape
@@ -134,13 +148,15 @@ def attention_fwd(q, k, v, scale, causal=False, window=(-1, -1), softcap=0.0,
                 rows = rows_all[c0:c0 + ROW_CHUNK]
                 z, _, ok = _row_block(qh, kh, rows, Sq, Sk, scale, causal, window, softcap, slope)
                 P, L = _softmax_rows(z, ok)
-                out[b, rows, h, :] = P @ vh
+                Pd, _ = _dropped(P, dropout, (b + batch0) * Hq + h, rows, np.arange(Sk))
+                out[b, rows, h, :] = Pd @ vh
                 lse[b, h, rows] = L
     return out, lse
 
 
 def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, heads=None, k_rows=None, q_rows=None, check_delta=True):
+                  alibi_slopes=None, heads=None, k_rows=None, q_rows=None, check_delta=True,
+                  dropout=None, batch0=0):
     """Analytic backward of standard attention in float64.
 
     The pages' method recomputes the attention matrix in the backward pass
@@ -156,6 +172,10 @@ def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0
       dv_j  = sum_{h in group} sum_i P_ij dO_i
 
     ALiBi and masks carry no gradient.  Returns (dq, dk, dv) float64.
+
+    With ``dropout`` (see ``attention_fwd``) the forward multiplies P by
+    M = K * scale before V, so dV uses P * M and dP_ij = M_ij (dO_i . v_j);
+    delta_i = sum_j P_ij dP_ij is still dO_i . O_i.
 
     ``heads`` restricts dq to those query heads and accumulates dk/dv only
     from them; ``k_rows`` restricts dk/dv to a subset of key rows (dq is then
@@ -185,32 +205,39 @@ def attention_bwd(q, k, v, dout, scale, causal=False, window=(-1, -1), softcap=0
                 rows = row_list[c0:c0 + ROW_CHUNK]
                 z, t, ok = _row_block(qh, kh, rows, Sq, Sk, scale, causal, window, softcap, slope)
                 P, _ = _softmax_rows(z, ok)
+                Pd, km = _dropped(P, dropout, (b + batch0) * Hq + h, rows, np.arange(Sk))
                 if q_rows is not None:
                     dP = doh[rows] @ vh.T
+                    if km is not None:
+                        dP = dP * km
                     delta = (P * dP).sum(axis=1)
                     dZ = P * (dP - delta[:, None])
                     dS = dZ * (1.0 - t * t) if t is not None else dZ
                     dq_h[rows] = scale * (dS @ kh)
                 elif k_rows is None:
                     dP = doh[rows] @ vh.T
+                    if km is not None:
+                        dP = dP * km
                     delta = (P * dP).sum(axis=1)
                     if check_delta:
-                        alt = (doh[rows] * (P @ vh)).sum(axis=1)
+                        alt = (doh[rows] * (Pd @ vh)).sum(axis=1)
                         assert np.allclose(delta, alt, rtol=1e-10, atol=1e-10)
                     dZ = P * (dP - delta[:, None])
                     dS = dZ * (1.0 - t * t) if t is not None else dZ
                     dq_h[rows] = scale * (dS @ kh)
                     dk[b, :, h // g, :] += scale * (dS.T @ qh[rows])
-                    dv[b, :, h // g, :] += P.T @ doh[rows]
+                    dv[b, :, h // g, :] += Pd.T @ doh[rows]
                 else:
-                    o_rows = P @ vh
+                    o_rows = Pd @ vh
                     delta = (doh[rows] * o_rows).sum(axis=1)
                     Pc = P[:, cols]
                     dPc = doh[rows] @ vh[cols].T
+                    if km is not None:
+                        dPc = dPc * km[:, cols]
                     dZ = Pc * (dPc - delta[:, None])
                     dS = dZ * (1.0 - t[:, cols] ** 2) if t is not None else dZ
                     dk[b, cols, h // g, :] += scale * (dS.T @ qh[rows])
-                    dv[b, cols, h // g, :] += Pc.T @ doh[rows]
+                    dv[b, cols, h // g, :] += Pd[:, cols].T @ doh[rows]
             if k_rows is None:
                 dq[b, :, h, :] = dq_h
     if q_rows is not None:

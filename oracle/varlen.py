@@ -20,8 +20,9 @@ def _cu(x):
 
 
 def varlen_fwd(q, k, v, cu_q, cu_k, scale, causal=False, window=(-1, -1), softcap=0.0,
-               alibi_slopes=None, seqs=None):
-    """Returns (out (total_q, Hq, D), lse (Hq, total_q)) in float64."""
+               alibi_slopes=None, seqs=None, dropout=None):
+    """Returns (out (total_q, Hq, D), lse (Hq, total_q)) in float64.  With
+    ``dropout`` the sequence index plays the batch entry of the mask."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cq, ck = _cu(cu_q), _cu(cu_k)
     tq, Hq, D = q.shape
@@ -32,14 +33,14 @@ def varlen_fwd(q, k, v, cu_q, cu_k, scale, causal=False, window=(-1, -1), softca
         if b2 == a:
             continue
         o, L = attention_fwd(q[None, a:b2], k[None, c:d], v[None, c:d], scale, causal, window,
-                             softcap, alibi_slopes)
+                             softcap, alibi_slopes, dropout=dropout, batch0=s)
         out[a:b2] = o[0]
         lse[:, a:b2] = L[0]
     return out, lse
 
 
 def varlen_bwd(q, k, v, dout, cu_q, cu_k, scale, causal=False, window=(-1, -1), softcap=0.0,
-               alibi_slopes=None, seqs=None):
+               alibi_slopes=None, seqs=None, dropout=None):
     """Returns (dq, dk, dv) packed like the inputs, float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     cq, ck = _cu(cu_q), _cu(cu_k)
@@ -54,6 +55,7 @@ def varlen_bwd(q, k, v, dout, cu_q, cu_k, scale, causal=False, window=(-1, -1), 
         if b2 == a:
             continue
         gq, gk, gv = attention_bwd(q[None, a:b2], k[None, c:d], v[None, c:d], do[None, a:b2],
-                                   scale, causal, window, softcap, alibi_slopes)
+                                   scale, causal, window, softcap, alibi_slopes,
+                                   dropout=dropout, batch0=s)
         dq[a:b2], dk[c:d], dv[c:d] = gq[0], gk[0], gv[0]
     return dq, dk, dv
