@@ -132,6 +132,59 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
 size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic);
 
 /*
+ * Dropout on the attention weights (the dropout_p argument of the attention
+ * call in section "上手 FlashAttention 的三步走" and in the interface listing
+ * of page "终极指南：如何通过FlashAttention实现Transformer模型的4倍加速与20倍内存优化").
+ * Same arguments and outputs as fa_fwd / fa_bwd / fa_fwd_varlen /
+ * fa_bwd_varlen, plus:
+ *   dropout_p in [0, 255.5/256): the drop probability, rounded to
+ *     t / 256 with t = round(256 p) (ties to even); t = 0 runs the plain
+ *     kernels.  Kept weights are scaled by 256 / (256 - t).
+ *   seed: 64-bit key of the counter-based generator Philox4x32-10
+ *     (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ *     1, 2, 3", SC 2011); offset: its low 32 bits are counter word 3, so
+ *     successive steps pass distinct offsets.
+ * Pair (query row i, key j) of batch entry b (varlen: sequence b; i, j
+ * counted within the sequence) and query head h is kept when byte j % 4 of
+ * word i % 4 of Philox4x32-10(counter = (j / 4, i / 4, b * Hq + h, offset),
+ * key = seed) is >= t.  out = (P * keep * 256 / (256 - t)) V; lse is that of
+ * the undropped weights.  The backward must get the same p, seed and offset
+ * as the forward; it regenerates the mask and stores nothing.
+ * Returns FA_ERR_INVALID_ARG for p outside the range or NaN.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                   float scale, int causal, int window_left, int window_right, float softcap,
+                   const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                   unsigned long long offset, void* stream);
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                   float scale, int causal, int window_left, int window_right, float softcap,
+                   const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                   unsigned long long offset, int deterministic,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                          int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                          int Hq, int Hkv, int D, int dtype,
+                          float scale, int causal, int window_left, int window_right, float softcap,
+                          const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                          unsigned long long offset, void* stream);
+
+int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                          int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                          int Hq, int Hkv, int D, int dtype,
+                          float scale, int causal, int window_left, int window_right, float softcap,
+                          const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                          unsigned long long offset, int deterministic,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Incremental decode against a (paged) KV cache (section "增量解码场景
  * flash_attn_with_kvcache"): the new k/v are appended to the cache in place
  * and the new queries attend over the cache plus the appended tokens.

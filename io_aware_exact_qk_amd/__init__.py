@@ -3,9 +3,11 @@
 The compute path is libfa.so (hand-written HIP kernels behind a C ABI,
 declared in include/fa.h); this package is its Python binding.
 """
-from .binding import (FAError, fa_bwd, fa_bwd_varlen, fa_fwd, fa_fwd_kvcache,  # noqa: F401
-                      fa_fwd_varlen, lib, profiler_disable, profiler_enable, profiler_read,
+from .binding import (FAError, fa_bwd, fa_bwd_dropout, fa_bwd_varlen,  # noqa: F401
+                      fa_bwd_varlen_dropout, fa_fwd, fa_fwd_dropout, fa_fwd_kvcache, fa_fwd_varlen,
+                      fa_fwd_varlen_dropout, lib, profiler_disable, profiler_enable, profiler_read,
                       profiler_reset)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_kvcache", "lib",
-           "FAError", "profiler_enable", "profiler_disable", "profiler_reset", "profiler_read"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_kvcache",
+           "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen_dropout", "fa_bwd_varlen_dropout",
+           "lib", "FAError", "profiler_enable", "profiler_disable", "profiler_reset", "profiler_read"]

@@ -61,6 +61,17 @@ def lib():
                                 _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
     L.fa_bwd_varlen_workspace_size.restype = _Z
     L.fa_bwd_varlen_workspace_size.argtypes = [_I] * 4
+    # dropout variants: the plain argument list with (p, seed, offset) in
+    # front of the stream (forward) or of `deterministic` (backward)
+    _D = [_F, ctypes.c_ulonglong, ctypes.c_ulonglong]
+    L.fa_fwd_dropout.restype = _I
+    L.fa_fwd_dropout.argtypes = L.fa_fwd.argtypes[:-1] + _D + [_P]
+    L.fa_bwd_dropout.restype = _I
+    L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:22] + _D + L.fa_bwd.argtypes[22:]
+    L.fa_fwd_varlen_dropout.restype = _I
+    L.fa_fwd_varlen_dropout.argtypes = L.fa_fwd_varlen.argtypes[:-1] + _D + [_P]
+    L.fa_bwd_varlen_dropout.restype = _I
+    L.fa_bwd_varlen_dropout.argtypes = L.fa_bwd_varlen.argtypes[:26] + _D + L.fa_bwd_varlen.argtypes[26:]
     L.fa_fwd_kvcache.restype = _I
     L.fa_fwd_kvcache.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I,
                                  _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
@@ -110,6 +121,11 @@ def _raise(fn, st):
         raise FAError(fn, st)
 
 
+def _drop(dropout_p, seed, offset):
+    """(p, seed, offset) as the dropout entry points take them."""
+    return [float(dropout_p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1)]
+
+
 def _opts(D, scale, window, softcap, alibi_slopes):
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     wl, wr = (int(window[0]), int(window[1]))
@@ -120,7 +136,7 @@ def _opts(D, scale, window, softcap, alibi_slopes):
 
 # -------------------------------------------------------------- forward ----
 def fa_fwd(q, k, v, out=None, lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
-           alibi_slopes=None, stream=None):
+           alibi_slopes=None, stream=None, _dropout=None):
     """q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D) -> (out (B,Sq,Hq,D), lse (B,Hq,Sq) float32)."""
     _check(q, "q", ndim=4)
     _check(k, "k", q.dtype, 4)
@@ -132,15 +148,24 @@ def fa_fwd(q, k, v, out=None, lse=None, scale=None, causal=False, window=(-1, -1
     out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
     lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
-    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, _dt(q),
-                      scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), _stream(stream))
-    _raise("fa_fwd", st)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, _dt(q),
+            scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes)]
+    if _dropout is None:
+        _raise("fa_fwd", lib().fa_fwd(*args, _stream(stream)))
+    else:
+        _raise("fa_fwd_dropout", lib().fa_fwd_dropout(*args, *_dropout, _stream(stream)))
     return out, lse
+
+
+def fa_fwd_dropout(q, k, v, dropout_p, seed, offset=0, **kw):
+    """fa_fwd with dropout on the attention weights (probability dropout_p,
+    Philox4x32-10 keyed by seed, counter word 3 = offset)."""
+    return fa_fwd(q, k, v, _dropout=_drop(dropout_p, seed, offset), **kw)
 
 
 def fa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale=None, causal=False,
            window=(-1, -1), softcap=0.0, alibi_slopes=None, deterministic=False, workspace=None,
-           stream=None):
+           stream=None, _dropout=None):
     """Gradients (dq, dk, dv) of attention given the forward's out and lse."""
     for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check(t, n, q.dtype, 4)
@@ -155,18 +180,27 @@ def fa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale=None, causa
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
-    st = L.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-                  _ptr(dv), B, Sq, Sk, Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc,
-                  _ptr(alibi_slopes), int(bool(deterministic)), _ptr(workspace),
-                  workspace.numel() * workspace.element_size(), _stream(stream))
-    _raise("fa_bwd", st)
+    head = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), B, Sq, Sk, Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc,
+            _ptr(alibi_slopes)]
+    tail = [int(bool(deterministic)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream)]
+    if _dropout is None:
+        _raise("fa_bwd", L.fa_bwd(*head, *tail))
+    else:
+        _raise("fa_bwd_dropout", L.fa_bwd_dropout(*head, *_dropout, *tail))
     return dq, dk, dv
+
+
+def fa_bwd_dropout(q, k, v, out, dout, lse, dropout_p, seed, offset=0, **kw):
+    """fa_bwd of fa_fwd_dropout: the same dropout_p, seed and offset."""
+    return fa_bwd(q, k, v, out, dout, lse, _dropout=_drop(dropout_p, seed, offset), **kw)
 
 
 # --------------------------------------------------------------- varlen ----
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out=None,
                   lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, stream=None):
+                  alibi_slopes=None, stream=None, _dropout=None):
     """Packed q (total_q,Hq,D), k/v (total_k,Hkv,D) -> (out, lse (Hq,total_q))."""
     _check(q, "q", ndim=3)
     _check(k, "k", q.dtype, 3)
@@ -181,17 +215,26 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
     lse = torch.empty(Hq, tq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
-    st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
-                             _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
-                             Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc,
-                             _ptr(alibi_slopes), _stream(stream))
-    _raise("fa_fwd_varlen", st)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+            _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
+            Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes)]
+    if _dropout is None:
+        _raise("fa_fwd_varlen", lib().fa_fwd_varlen(*args, _stream(stream)))
+    else:
+        _raise("fa_fwd_varlen_dropout", lib().fa_fwd_varlen_dropout(*args, *_dropout, _stream(stream)))
     return out, lse
+
+
+def fa_fwd_varlen_dropout(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          dropout_p, seed, offset=0, **kw):
+    """fa_fwd_varlen with dropout; sequence s plays the mask's batch entry."""
+    return fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                         _dropout=_drop(dropout_p, seed, offset), **kw)
 
 
 def fa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                   dq=None, dk=None, dv=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, deterministic=False, workspace=None, stream=None):
+                  alibi_slopes=None, deterministic=False, workspace=None, stream=None, _dropout=None):
     for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check(t, n, q.dtype, 3)
     _check(lse, "lse", torch.float32, 2)
@@ -206,13 +249,24 @@ def fa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
-    st = L.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
-                         _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq,
-                         int(max_seqlen_q), int(max_seqlen_k), tq, tk, Hq, Hkv, D, _dt(q), scale,
-                         int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), int(bool(deterministic)),
-                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    _raise("fa_bwd_varlen", st)
+    head = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq,
+            int(max_seqlen_q), int(max_seqlen_k), tq, tk, Hq, Hkv, D, _dt(q), scale,
+            int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes)]
+    tail = [int(bool(deterministic)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream)]
+    if _dropout is None:
+        _raise("fa_bwd_varlen", L.fa_bwd_varlen(*head, *tail))
+    else:
+        _raise("fa_bwd_varlen_dropout", L.fa_bwd_varlen_dropout(*head, *_dropout, *tail))
     return dq, dk, dv
+
+
+def fa_bwd_varlen_dropout(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                          max_seqlen_k, dropout_p, seed, offset=0, **kw):
+    """fa_bwd_varlen of fa_fwd_varlen_dropout (same dropout_p, seed, offset)."""
+    return fa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                         max_seqlen_k, _dropout=_drop(dropout_p, seed, offset), **kw)
 
 
 # -------------------------------------------------------------- kvcache ----

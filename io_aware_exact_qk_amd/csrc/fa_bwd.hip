@@ -51,6 +51,7 @@ struct BwdParams {
   int wl, wr;
   int n_tiles, n_heads, n_batch, reverse, balanced;
   int n_tokens;  // preprocess: number of (token) rows
+  DropSpec drop; // DROP kernels only
 };
 
 // dK/dV work-group: this many waves of 32 keys each (two waves per SIMD).
@@ -145,7 +146,7 @@ __device__ __forceinline__ float softcap_grad(float ds, float pv, float x, int i
 // the VGPRs two waves per SIMD need).  Query tiles of 64 rows (Q, dO, LSE,
 // delta) are copied into LDS by DMA, double buffered; the copy of tile n+1
 // runs under the matrix work of tile n.
-template <int D, int DT, bool SOFTCAP, bool ALIBI>
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = DKDV_WAVES, BC = 32 * NW, BR = 64;
   constexpr int KC = D / 16, DB = D / 32;
@@ -253,6 +254,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             s[ii] = ok ? s[ii] : -INFINITY;
           }
         }
+        // dropout: kept weights enter dV and dP (scaled once at the end / here)
+        uint32_t kx[4];
+        if constexpr (DROP) drop_words<true>(p.drop, (uint32_t)(b * p.Hq + hq), my_key, r0, lane, kx);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 32 * rb + 8 * qd + 4 * g);
@@ -261,11 +265,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int ii = 4 * qd + e;
             const float pv = fast_exp2(fmaf(s[ii], fs, -l4[e]));
-            float ds = pv * (dp[ii] - d4[e]);
+            bool keep = true;
+            float dpv = dp[ii];
+            if constexpr (DROP) {
+              keep = drop_keep(kx, ii, p.drop.t);
+              dpv = keep ? dpv * p.drop.scale : 0.0f;
+            }
+            float ds = pv * (dpv - d4[e]);
             if constexpr (SOFTCAP) {
               ds = softcap_grad<ALIBI>(ds, pv, s[ii], r0 + frag_row(ii, g) + off, my_key, p, slope_log2);
             }
-            s[ii] = pv;
+            s[ii] = keep ? pv : 0.0f;
             dp[ii] = ds;
           }
         }
@@ -308,8 +318,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
         u32x2 a, c;
         a[0] = pack2<DT>(dkacc[d][4 * qd + 0] * p.scale, dkacc[d][4 * qd + 1] * p.scale);
         a[1] = pack2<DT>(dkacc[d][4 * qd + 2] * p.scale, dkacc[d][4 * qd + 3] * p.scale);
-        c[0] = pack2<DT>(dvacc[d][4 * qd + 0], dvacc[d][4 * qd + 1]);
-        c[1] = pack2<DT>(dvacc[d][4 * qd + 2], dvacc[d][4 * qd + 3]);
+        const float vs = DROP ? p.drop.scale : 1.0f;
+        c[0] = pack2<DT>(dvacc[d][4 * qd + 0] * vs, dvacc[d][4 * qd + 1] * vs);
+        c[1] = pack2<DT>(dvacc[d][4 * qd + 2] * vs, dvacc[d][4 * qd + 3] * vs);
         gstore64(dkrow + 32 * d + 8 * qd + 4 * g, a);
         gstore64(dvrow + 32 * d + 8 * qd + 4 * g, c);
       }
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 // Work-group = 128 query rows of one query head (4 waves of 32 rows), two
 // work-groups per CU; K/V tiles of 64 keys are copied into LDS by DMA,
 // double buffered.
-template <int D, int DT, bool SOFTCAP, bool ALIBI>
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16, DB = D / 32;
@@ -414,6 +425,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          uint32_t kx[4];
+          if constexpr (DROP) drop_words<false>(p.drop, (uint32_t)(b * p.Hq + h), my_row, j0 + 32 * kb, lane, kx);
           // logits, mask (keys past Sk hold a copy of the last key), P and dS
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -422,7 +435,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
             if constexpr (SOFTCAP || ALIBI) x = logit2<SOFTCAP, ALIBI>(x, ip, j, p, slope_log2);
             if constexpr (MASKED) x = (row_ok & visible(ip, j, Sk, mask)) ? x : -INFINITY;
             const float pv = fast_exp2(fmaf(x, fs, -lse2));
-            float ds = pv * (dp[kb][i] - dv_row);
+            float dpv = dp[kb][i];
+            if constexpr (DROP) dpv = drop_keep(kx, i, p.drop.t) ? dpv * p.drop.scale : 0.0f;
+            float ds = pv * (dpv - dv_row);
             if constexpr (SOFTCAP) ds = softcap_grad<ALIBI>(ds, pv, x, ip, j, p, slope_log2);
             dp[kb][i] = ds;
           }
@@ -471,18 +486,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------- dispatch ---
-template <int D, int DT, bool SC, bool AL>
+template <int D, int DT, bool SC, bool AL, bool DR>
 static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
   if (nwg_kv > 0) {
     prof_before(FA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL>), dim3(nwg_kv), dim3(64 * DKDV_WAVES), 0, st, dkdv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR>), dim3(nwg_kv), dim3(64 * DKDV_WAVES), 0, st, dkdv);
     prof_after(FA_KERNEL_BWD_DKDV, st);
   }
   if (nwg_q > 0) {
     prof_before(FA_KERNEL_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL>), dim3(nwg_q), dim3(256), 0, st, dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL, DR>), dim3(nwg_q), dim3(256), 0, st, dq);
     prof_after(FA_KERNEL_BWD_DQ, st);
   }
+}
+
+template <int D, int DT, bool SC, bool AL>
+static void launch_main_d(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, bool dr,
+                          hipStream_t st) {
+  if (dr) launch_main<D, DT, SC, AL, true>(dkdv, dq, nwg_kv, nwg_q, st);
+  else launch_main<D, DT, SC, AL, false>(dkdv, dq, nwg_kv, nwg_q, st);
 }
 
 template <int D, int DT>
@@ -493,12 +515,13 @@ static void launch_all(const BwdParams& pre, int nwg_pre, const BwdParams& dkdv,
     hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3(nwg_pre), dim3(256), 0, st, pre);
     prof_after(FA_KERNEL_BWD_PREPROCESS, st);
   }
+  const bool dr = dkdv.drop.t > 0;
   if (sc) {
-    if (al) launch_main<D, DT, true, true>(dkdv, dq, nwg_kv, nwg_q, st);
-    else launch_main<D, DT, true, false>(dkdv, dq, nwg_kv, nwg_q, st);
+    if (al) launch_main_d<D, DT, true, true>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    else launch_main_d<D, DT, true, false>(dkdv, dq, nwg_kv, nwg_q, dr, st);
   } else {
-    if (al) launch_main<D, DT, false, true>(dkdv, dq, nwg_kv, nwg_q, st);
-    else launch_main<D, DT, false, false>(dkdv, dq, nwg_kv, nwg_q, st);
+    if (al) launch_main_d<D, DT, false, true>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    else launch_main_d<D, DT, false, false>(dkdv, dq, nwg_kv, nwg_q, dr, st);
   }
 }
 
@@ -587,12 +610,12 @@ extern "C" size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int d
   return 2 * align_up((size_t)total_q * Hq * sizeof(float), 256);
 }
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv,
-                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
-                      float scale, int causal, int window_left, int window_right, float softcap,
-                      const float* alibi_slopes, int deterministic,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+static int bwd_dense(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                     float scale, int causal, int window_left, int window_right, float softcap,
+                     const float* alibi_slopes, const DropSpec& drop, int deterministic,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
@@ -606,17 +629,18 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   p.lse2 = (float*)((char*)workspace + need / 2);
   p.Sq = Sq;
   p.Sk = Sk;
+  p.drop = drop;
   return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, B * Sq, causal, (hipStream_t)stream);
 }
 
-extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                             const float* lse, void* dq, void* dk, void* dv,
-                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
-                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                             int Hq, int Hkv, int D, int dtype,
-                             float scale, int causal, int window_left, int window_right, float softcap,
-                             const float* alibi_slopes, int deterministic,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+static int bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                      int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                      int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, const DropSpec& drop, int deterministic,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
@@ -633,5 +657,62 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
+  p.drop = drop;
   return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, total_q, causal, (hipStream_t)stream);
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, int deterministic,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_dense(q, k, v, out, dout, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
+                   window_left, window_right, softcap, alibi_slopes, DropSpec{}, deterministic, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv,
+                              int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                              float scale, int causal, int window_left, int window_right, float softcap,
+                              const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                              unsigned long long offset, int deterministic,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  DropSpec drop;
+  if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
+  return bwd_dense(q, k, v, out, dout, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
+                   window_left, window_right, softcap, alibi_slopes, drop, deterministic, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                             int Hq, int Hkv, int D, int dtype,
+                             float scale, int causal, int window_left, int window_right, float softcap,
+                             const float* alibi_slopes, int deterministic,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_varlen(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q,
+                    max_seqlen_k, total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left,
+                    window_right, softcap, alibi_slopes, DropSpec{}, deterministic, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                     const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                                     int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                                     int Hq, int Hkv, int D, int dtype,
+                                     float scale, int causal, int window_left, int window_right,
+                                     float softcap, const float* alibi_slopes, float dropout_p,
+                                     unsigned long long seed, unsigned long long offset, int deterministic,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  DropSpec drop;
+  if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
+  return bwd_varlen(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q,
+                    max_seqlen_k, total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left,
+                    window_right, softcap, alibi_slopes, drop, deterministic, workspace, workspace_bytes,
+                    stream);
 }

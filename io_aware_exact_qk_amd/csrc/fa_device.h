@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_host.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -328,6 +330,102 @@ __device__ __forceinline__ int classify(int ip0, int ip1, int j0, int j1, int Sk
   if (m.wl >= 0 && j1 < ip0 - m.wl) return 0;
   const bool full = (j1 < Sk) && (m.wr < 0 || j1 <= ip0 + m.wr) && (m.wl < 0 || j0 >= ip1 - m.wl);
   return full ? 2 : 1;
+}
+
+// ------------------------------------------------------------- dropout ----
+// Dropout on the attention weights.  The keep decision of (query row i, key
+// j) of one (batch entry, query head) bh comes from the counter-based
+// generator Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror,
+// D. E. Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): one
+// call per 4 x 4 block of pairs, counter (j/4, i/4, bh, offset), key = the
+// 64-bit seed; word i%4 of the result holds the block's row i, byte j%4 of
+// that word the pair (i, j), which is kept when the byte is >= t.  Kept
+// weights are scaled by 256 / (256 - t), applied once to the accumulated
+// products.
+// (DropSpec, the parameters, is declared with the host helpers.)
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// 4 x 4 transpose across the four lanes of every quad: word w of lane q
+// becomes word q of lane w.  Stage 1 exchanges lane bit 0 with word bit 0
+// (DPP quad_perm [1,0,3,2]), stage 2 lane bit 1 with word bit 1
+// (quad_perm [2,3,0,1]).
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int lane) {
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+#pragma unroll
+  for (int w = 0; w < 4; w += 2) {
+    const uint32_t send = b0 ? x[w] : x[w + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    if (b0) x[w] = recv;
+    else x[w + 1] = recv;
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t send = b1 ? x[w] : x[w + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);
+    if (b1) x[w] = recv;
+    else x[w + 2] = recv;
+  }
+}
+
+// 4 x 4 byte transpose inside one lane: byte c of word a becomes byte a of
+// word c.  v_perm_b32 picks each result byte from the 8 bytes {s0 : s1}
+// (s1 = bytes 0..3, s0 = bytes 4..7).
+__device__ __forceinline__ void byte_transpose(uint32_t (&x)[4]) {
+  const uint32_t a0 = __builtin_amdgcn_perm(x[1], x[0], 0x06020400u);  // x0.0 x1.0 x0.2 x1.2
+  const uint32_t a1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030501u);  // x0.1 x1.1 x0.3 x1.3
+  const uint32_t c0 = __builtin_amdgcn_perm(x[3], x[2], 0x06020400u);  // x2.0 x3.0 x2.2 x3.2
+  const uint32_t c1 = __builtin_amdgcn_perm(x[3], x[2], 0x07030501u);  // x2.1 x3.1 x2.3 x3.3
+  x[0] = __builtin_amdgcn_perm(c0, a0, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(c1, a1, 0x05040100u);
+  x[2] = __builtin_amdgcn_perm(c0, a0, 0x07060302u);
+  x[3] = __builtin_amdgcn_perm(c1, a1, 0x07060302u);
+}
+
+// Keep words of a 32 x 32 block in MFMA accumulator layout.  A lane owns one
+// index `own` along the accumulator's columns (a query, or a key) and the
+// runs R = 0..3 of four consecutive indices 8 R + 4 g + 0..3 along its rows,
+// counted from `first`.  The four lanes of a quad own four consecutive
+// indices (own % 4 = lane % 4); lane q computes the generator call of run q.
+// Queries along the columns: the call's word own % 4 is the lane's, so the
+// quad transpose hands lane q word q of every run's call.  Keys along the
+// columns: the call of run R holds the four queries as words and the quad's
+// keys as bytes; a byte transpose first gathers byte (own % 4) of the four
+// words.  Either way x[R] byte c keeps the pair at row 8 R + 4 g + c.
+template <bool KEY_COLUMNS>
+__device__ __forceinline__ void drop_words(const DropSpec& ds, uint32_t bh, int own, int first, int lane,
+                                           uint32_t (&x)[4]) {
+  const int run = lane & 3, g = (lane >> 5) & 1;
+  const uint32_t row4 = (uint32_t)(first + 8 * run + 4 * g) >> 2;
+  const uint32_t own4 = (uint32_t)own >> 2;
+  // counter = (key / 4, query / 4, bh, offset)
+  const u32x4 w = KEY_COLUMNS ? philox4x32_10(own4, row4, bh, ds.off, ds.k0, ds.k1)
+                              : philox4x32_10(row4, own4, bh, ds.off, ds.k0, ds.k1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = w[e];
+  if constexpr (KEY_COLUMNS) byte_transpose(x);
+  quad_transpose(x, lane);
+}
+
+// Element e (0..15) of the lane's accumulator fragment: kept?
+__device__ __forceinline__ bool drop_keep(const uint32_t (&x)[4], int e, uint32_t t) {
+  return ((x[e >> 2] >> (8 * (e & 3))) & 0xFFu) >= t;
 }
 
 }  // namespace fa

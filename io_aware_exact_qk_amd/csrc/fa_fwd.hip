@@ -47,9 +47,10 @@ struct FwdParams {
   int wl, wr;           // window, causal folded into wr = 0
   int n_qtiles, n_heads, n_batch;
   int reverse;          // causal: heaviest tiles first
+  DropSpec drop;        // DROP kernels only
 };
 
-template <int D, int DT, bool SOFTCAP, bool ALIBI>
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16;               // MFMA steps along D
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
+  const uint32_t bh = (uint32_t)(b * p.Hq + h);  // dropout counter word 2
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
@@ -185,16 +187,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       return (m_run == -INFINITY) ? 0.0f : m_run;
     };
 
-    // P = 2^(x - m) as four 16-bit B operands (acc-order), row sums into l_run.
-    auto expo = [&](f32x16 (&sa)[2], float m_use, u32x4 (&pb)[4]) {
+    // Dropout keep words of tile t (two 32-key halves).
+    auto keepw = [&](int t, uint32_t (&kw)[2][4]) {
+      if constexpr (DROP) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) drop_words<false>(p.drop, bh, my_row, t * BC + 32 * kb, lane, kw[kb]);
+      }
+    };
+
+    // P = 2^(x - m) as four 16-bit B operands (acc-order), row sums into l_run
+    // (dropped weights count in the sum and enter the product as 0).
+    auto expo = [&](f32x16 (&sa)[2], float m_use, const uint32_t (&kw)[2][4], u32x4 (&pb)[4]) {
       float lsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = fast_exp2(fmaf(sa[kb][i], fs, -m_use));
-          sa[kb][i] = pv;
           lsum += pv;
+          sa[kb][i] = (DROP && !drop_keep(kw[kb], i, p.drop.t)) ? 0.0f : pv;
         }
       l_run += lsum;
 #pragma unroll
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // down next to its MFMA, which would expose the whole LDS latency on
     // every MFMA.
     auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, f32x16 (&sc)[2],
-                     f32x16 (&sn)[2], float m_use) {
+                     f32x16 (&sn)[2], float m_use, const uint32_t (&kw)[2][4]) {
       constexpr int NS = 2 * KC;    // S MFMAs per tile
       constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
       u32x4 kr[4];
@@ -240,8 +251,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         for (int e = 0; e < EPS; ++e) {
           const int idx = i * EPS + e;
           const float pv = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
-          sc[idx >> 4][idx & 15] = pv;
           lsum += pv;
+          sc[idx >> 4][idx & 15] = (DROP && !drop_keep(kw[idx >> 4], idx & 15, p.drop.t)) ? 0.0f : pv;
         }
         if (((i + 1) * EPS) % 8 == 0) {
           const int mk = (i + 1) * EPS / 8 - 1;
@@ -273,8 +284,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       if (t + 2 < t_hi) dma_k(t + 2, kdst);
       dma_v(t + 1, vdst);
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
+      uint32_t kw[2][4];
+      keepw(t, kw);
       const float m_use = prep(t, sc);
-      fused(kn, vt, nbv, tbv, sc, sn, m_use);
+      fused(kn, vt, nbv, tbv, sc, sn, m_use, kw);
       dma_wait();
       __syncthreads();
     };
@@ -282,15 +295,43 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // Final tile: no next S, no DMA.
     auto last = [&](int t, const char* vt, f32x16 (&sc)[2]) {
       const uint32_t tbv = opaque(tb);
+      uint32_t kw[2][4];
+      keepw(t, kw);
       const float m_use = prep(t, sc);
       u32x4 pb[4];
-      expo(sc, m_use, pb);
+      expo(sc, m_use, kw, pb);
       pv(vt, tbv, pb);
     };
 
     // Four distinct LDS arrays: K and V, double buffered, so reads of one are
     // never ordered behind the DMA into another.
     f32x16 sA[2], sB[2];
+    if constexpr (DROP) {
+      // With dropout the generator's integer work dominates the VALU, so the
+      // tiles run one after another (S, softmax, P V) with the next tile's
+      // K and V copied in underneath; this keeps the keep words in registers
+      // without spilling.
+      auto plain = [&](int t, const char* kt, const char* vt, char* kdst, char* vdst) {
+        if (t + 1 < t_hi) {
+          dma_k(t + 1, kdst);
+          dma_v(t + 1, vdst);
+        }
+        qk(kt, opaque(nb), sA);
+        last(t, vt, sA);
+        dma_wait();
+        __syncthreads();
+      };
+      dma_k(t_lo, kb0);
+      dma_v(t_lo, vb0);
+      dma_wait();
+      __syncthreads();
+      int t = t_lo;
+      for (; t + 1 < t_hi; t += 2) {
+        plain(t, kb0, vb0, kb1, vb1);
+        plain(t + 1, kb1, vb1, kb0, vb0);
+      }
+      if (t < t_hi) plain(t, kb0, vb0, kb1, vb1);
+    } else {
     dma_k(t_lo, kb0);
     dma_v(t_lo, vb0);
     if (t_lo + 1 < t_hi) dma_k(t_lo + 1, kb1);
@@ -309,12 +350,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     } else {
       last(t, vb0, sA);
     }
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float l_tot = l_run + xor32(l_run);
   if (row_ok) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) / l_tot : 0.0f;
     uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.q_rstride + h * D;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
@@ -335,16 +377,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, int DT>
+template <int D, int DT, bool DROP>
 static void launch_fwd_dt(const FwdParams& prm, bool softcap, bool alibi, int nwg, hipStream_t st) {
   dim3 grid(nwg), block(256);
   if (softcap) {
-    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, true, true>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((fwd_kernel<D, DT, true, false>), grid, block, 0, st, prm);
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, true, true, DROP>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, true, false, DROP>), grid, block, 0, st, prm);
   } else {
-    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, false, true>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((fwd_kernel<D, DT, false, false>), grid, block, 0, st, prm);
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, false, true, DROP>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, false, false, DROP>), grid, block, 0, st, prm);
   }
+}
+
+template <int D, int DT>
+static void launch_fwd_d(const FwdParams& prm, bool softcap, bool alibi, bool drop, int nwg, hipStream_t st) {
+  if (drop) launch_fwd_dt<D, DT, true>(prm, softcap, alibi, nwg, st);
+  else launch_fwd_dt<D, DT, false>(prm, softcap, alibi, nwg, st);
 }
 
 static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap, int causal,
@@ -360,27 +408,23 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
   const long long nwg = (long long)prm.n_qtiles * prm.n_heads * prm.n_batch;
   if (nwg <= 0) return FA_OK;
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
-  const bool sc = softcap > 0.0f, al = prm.alibi != nullptr;
+  const bool sc = softcap > 0.0f, al = prm.alibi != nullptr, dr = prm.drop.t > 0;
   prof_before(FA_KERNEL_FWD, st);
   if (D == 128) {
-    if (dtype == FA_DTYPE_BF16) launch_fwd_dt<128, DT_BF16>(prm, sc, al, (int)nwg, st);
-    else launch_fwd_dt<128, DT_F16>(prm, sc, al, (int)nwg, st);
+    if (dtype == FA_DTYPE_BF16) launch_fwd_d<128, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+    else launch_fwd_d<128, DT_F16>(prm, sc, al, dr, (int)nwg, st);
   } else {
-    if (dtype == FA_DTYPE_BF16) launch_fwd_dt<64, DT_BF16>(prm, sc, al, (int)nwg, st);
-    else launch_fwd_dt<64, DT_F16>(prm, sc, al, (int)nwg, st);
+    if (dtype == FA_DTYPE_BF16) launch_fwd_d<64, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+    else launch_fwd_d<64, DT_F16>(prm, sc, al, dr, (int)nwg, st);
   }
   prof_after(FA_KERNEL_FWD, st);
   return launch_status();
 }
 
-}  // namespace fa
-
-using namespace fa;
-
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
-                      float scale, int causal, int window_left, int window_right, float softcap,
-                      const float* alibi_slopes, void* stream) {
+static int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                     float scale, int causal, int window_left, int window_right, float softcap,
+                     const float* alibi_slopes, const DropSpec& drop, void* stream) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
@@ -402,15 +446,16 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* out, fl
   prm.alibi = alibi_slopes;
   prm.wl = window_left;
   prm.wr = window_right;
+  prm.drop = drop;
   return run_fwd(prm, D, dtype, scale, softcap, causal, Sq, B, (hipStream_t)stream);
 }
 
-extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
-                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
-                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                             int Hq, int Hkv, int D, int dtype,
-                             float scale, int causal, int window_left, int window_right, float softcap,
-                             const float* alibi_slopes, void* stream) {
+static int fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                      int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                      int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, const DropSpec& drop, void* stream) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
@@ -435,5 +480,54 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   prm.alibi = alibi_slopes;
   prm.wl = window_left;
   prm.wr = window_right;
+  prm.drop = drop;
   return run_fwd(prm, D, dtype, scale, softcap, causal, max_seqlen_q, nseq, (hipStream_t)stream);
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                      float scale, int causal, int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, void* stream) {
+  return fwd_dense(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal, window_left,
+                   window_right, softcap, alibi_slopes, DropSpec{}, stream);
+}
+
+extern "C" int fa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                              float scale, int causal, int window_left, int window_right, float softcap,
+                              const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                              unsigned long long offset, void* stream) {
+  DropSpec drop;
+  if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
+  return fwd_dense(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal, window_left,
+                   window_right, softcap, alibi_slopes, drop, stream);
+}
+
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                             int Hq, int Hkv, int D, int dtype,
+                             float scale, int causal, int window_left, int window_right, float softcap,
+                             const float* alibi_slopes, void* stream) {
+  return fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k,
+                    total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left, window_right, softcap,
+                    alibi_slopes, DropSpec{}, stream);
+}
+
+extern "C" int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                                     int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                                     int Hq, int Hkv, int D, int dtype,
+                                     float scale, int causal, int window_left, int window_right,
+                                     float softcap, const float* alibi_slopes, float dropout_p,
+                                     unsigned long long seed, unsigned long long offset, void* stream) {
+  DropSpec drop;
+  if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
+  return fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k,
+                    total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left, window_right, softcap,
+                    alibi_slopes, drop, stream);
 }

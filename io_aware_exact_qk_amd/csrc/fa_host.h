@@ -29,6 +29,29 @@ inline int check_common(int Hq, int Hkv, int D, int dtype, float scale, int wl, 
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Dropout parameters of one call (see the dropout section of fa_device.h).
+struct DropSpec {
+  uint32_t k0, k1;  // seed, low and high word
+  uint32_t off;     // counter word 3
+  uint32_t t;       // byte threshold, round(256 p); 0 = no dropout
+  float scale;      // 256 / (256 - t)
+};
+
+// Dropout parameters: p in [0, 255.5/256), finite.  The byte threshold is
+// t = round(256 p) with ties to even (the default rounding mode of lrint);
+// t = 0 means no dropout.  The seed is the generator key, the low word of
+// the offset its counter word 3.
+inline bool make_drop(float p, unsigned long long seed, unsigned long long offset, DropSpec& d) {
+  if (!(p >= 0.0f) || !(p < 255.5f / 256.0f)) return false;
+  const long t = lrintf(p * 256.0f);
+  d.k0 = (uint32_t)(seed & 0xffffffffull);
+  d.k1 = (uint32_t)(seed >> 32);
+  d.off = (uint32_t)(offset & 0xffffffffull);
+  d.t = (uint32_t)t;
+  d.scale = 256.0f / (float)(256 - t);
+  return true;
+}
+
 // Work-group ids are handed to the 8 XCDs round-robin (id % 8).
 struct TileId {
   int t, h, b;  // tile index along the sequence, head, batch entry

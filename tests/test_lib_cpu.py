@@ -76,6 +76,14 @@ def test_fwd_rejects_invalid(lib, kw, status):
     assert _fwd(lib, **kw) == status
 
 
+@pytest.mark.parametrize("p", [1.0, -0.01, float("nan"), 255.5 / 256])
+def test_dropout_rejects_probability(lib, p):
+    st = lib.fa_fwd_dropout(F, F, F, F, F, 1, 8, 8, 2, 2, 128, 1, ctypes.c_float(0.1), 0, -1, -1,
+                            ctypes.c_float(0.0), None, ctypes.c_float(p), ctypes.c_ulonglong(1),
+                            ctypes.c_ulonglong(0), None)
+    assert st == 1
+
+
 def test_bwd_rejects_small_workspace(lib):
     st = lib.fa_bwd(F, F, F, F, F, F, F, F, F, 1, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, 0,
                     F, 16, None)
