@@ -139,6 +139,29 @@ def run_fwdbwd(args, torch, fa):
             fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
             per.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
                         "tflops": round(fl / ms / 1e9, 1)})
+    # dropout (p = 0.1) on the long sequences, reported beside the headline
+    drop = []
+    for t in cases:
+        if t["S"] < 4096:
+            continue
+        for causal in (False, True):
+            def one_drop():
+                fa.fa_fwd_dropout(t["q"], t["k"], t["v"], 0.1, 1234, 0, out=t["out"], lse=t["lse"],
+                                  scale=scale, causal=causal)
+                fa.fa_bwd_dropout(t["q"], t["k"], t["v"], t["out"], t["do"], t["lse"], 0.1, 1234, 0,
+                                  dq=t["dq"], dk=t["dk"], dv=t["dv"], scale=scale, causal=causal,
+                                  workspace=t["ws"])
+            one_drop()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                one_drop()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 3
+            fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
+            drop.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
+                         "tflops": round(fl / ms / 1e9, 1)})
     # timed region
     fa.profiler_enable(4096)
     fa.profiler_reset()
@@ -170,7 +193,7 @@ def run_fwdbwd(args, torch, fa):
                 "traffic": recorded_traffic(dom),
                 "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
     return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
-                roofline=roofline, flops_step=flops_step)
+                roofline=roofline, flops_step=flops_step, dropout=drop)
 
 
 # ---------------------------------------------------------------------------
@@ -384,6 +407,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": fb["kernels"],
         "per_config": fb["per_config"],
+        "dropout_p0.1": fb["dropout"],
         "decode": dec,
     }
     print(json.dumps(line))
