@@ -132,6 +132,38 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
 size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic);
 
 /*
+ * Packed layouts (section "上手 FlashAttention 的三步走": when Q, K and V are
+ * already packed into one tensor, the qkvpacked call is the faster route).
+ *   fa_*_qkvpacked: qkv (B, S, 3, H, D) in -- q, k, v interleaved per token,
+ *     so Sq = Sk = S and Hq = Hkv = H; dqkv (B, S, 3, H, D) out.
+ *   fa_*_kvpacked: q (B, Sq, Hq, D), kv (B, Sk, 2, Hkv, D); dkv likewise.
+ *   out, dout (B, Sq, Hq, D) and lse are laid out as for fa_fwd / fa_bwd.
+ * Same kernels as fa_fwd / fa_bwd, reading and writing with the packed row
+ * strides; same options, results and workspace (fa_bwd_workspace_size).
+ */
+int fa_fwd_qkvpacked(const void* qkv, void* out, float* lse, int B, int S, int H, int D, int dtype,
+                     float scale, int causal, int window_left, int window_right, float softcap,
+                     const float* alibi_slopes, void* stream);
+
+int fa_bwd_qkvpacked(const void* qkv, const void* out, const void* dout, const float* lse,
+                     void* dqkv, int B, int S, int H, int D, int dtype,
+                     float scale, int causal, int window_left, int window_right, float softcap,
+                     const float* alibi_slopes, int deterministic,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+int fa_fwd_kvpacked(const void* q, const void* kv, void* out, float* lse,
+                    int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                    float scale, int causal, int window_left, int window_right, float softcap,
+                    const float* alibi_slopes, void* stream);
+
+int fa_bwd_kvpacked(const void* q, const void* kv, const void* out, const void* dout,
+                    const float* lse, void* dq, void* dkv,
+                    int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                    float scale, int causal, int window_left, int window_right, float softcap,
+                    const float* alibi_slopes, int deterministic,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dropout on the attention weights (the dropout_p argument of the attention
  * call in section "上手 FlashAttention 的三步走" and in the interface listing
  * of page "终极指南：如何通过FlashAttention实现Transformer模型的4倍加速与20倍内存优化").

@@ -70,6 +70,16 @@ def lib():
     L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:22] + _D + L.fa_bwd.argtypes[22:]
     L.fa_fwd_varlen_dropout.restype = _I
     L.fa_fwd_varlen_dropout.argtypes = L.fa_fwd_varlen.argtypes[:-1] + _D + [_P]
+    L.fa_fwd_qkvpacked.restype = _I
+    L.fa_fwd_qkvpacked.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _P]
+    L.fa_bwd_qkvpacked.restype = _I
+    L.fa_bwd_qkvpacked.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _I,
+                                   _P, _Z, _P]
+    L.fa_fwd_kvpacked.restype = _I
+    L.fa_fwd_kvpacked.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _P]
+    L.fa_bwd_kvpacked.restype = _I
+    L.fa_bwd_kvpacked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                                  _F, _P, _I, _P, _Z, _P]
     L.fa_bwd_varlen_dropout.restype = _I
     L.fa_bwd_varlen_dropout.argtypes = L.fa_bwd_varlen.argtypes[:26] + _D + L.fa_bwd_varlen.argtypes[26:]
     L.fa_fwd_kvcache.restype = _I
@@ -195,6 +205,87 @@ def fa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale=None, causa
 def fa_bwd_dropout(q, k, v, out, dout, lse, dropout_p, seed, offset=0, **kw):
     """fa_bwd of fa_fwd_dropout: the same dropout_p, seed and offset."""
     return fa_bwd(q, k, v, out, dout, lse, _dropout=_drop(dropout_p, seed, offset), **kw)
+
+
+# --------------------------------------------------------------- packed ----
+def fa_fwd_qkvpacked(qkv, out=None, lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
+                     alibi_slopes=None, stream=None):
+    """qkv (B,S,3,H,D) -> (out (B,S,H,D), lse (B,H,S) float32)."""
+    _check(qkv, "qkv", ndim=5)
+    B, S, three, H, D = qkv.shape
+    if three != 3:
+        raise ValueError("qkv must be (B, S, 3, H, D)")
+    out = torch.empty(B, S, H, D, device=qkv.device, dtype=qkv.dtype) if out is None else _check(out, "out", qkv.dtype)
+    lse = torch.empty(B, H, S, device=qkv.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = lib().fa_fwd_qkvpacked(_ptr(qkv), _ptr(out), _ptr(lse), B, S, H, D, _dt(qkv), scale,
+                                int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), _stream(stream))
+    _raise("fa_fwd_qkvpacked", st)
+    return out, lse
+
+
+def fa_bwd_qkvpacked(qkv, out, dout, lse, dqkv=None, scale=None, causal=False, window=(-1, -1),
+                     softcap=0.0, alibi_slopes=None, deterministic=False, workspace=None, stream=None):
+    """Gradient dqkv (B,S,3,H,D) of fa_fwd_qkvpacked."""
+    _check(qkv, "qkv", ndim=5)
+    B, S, _, H, D = qkv.shape
+    _check(out, "out", qkv.dtype, 4)
+    _check(dout, "dout", qkv.dtype, 4)
+    _check(lse, "lse", torch.float32, 3)
+    dqkv = torch.empty_like(qkv) if dqkv is None else _check(dqkv, "dqkv", qkv.dtype)
+    L = lib()
+    ws_bytes = L.fa_bwd_workspace_size(B, S, S, H, H, D, int(bool(deterministic)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=qkv.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_bwd_qkvpacked(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dqkv), B, S, H, D, _dt(qkv),
+                            scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), int(bool(deterministic)),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("fa_bwd_qkvpacked", st)
+    return dqkv
+
+
+def fa_fwd_kvpacked(q, kv, out=None, lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
+                    alibi_slopes=None, stream=None):
+    """q (B,Sq,Hq,D), kv (B,Sk,2,Hkv,D) -> (out, lse)."""
+    _check(q, "q", ndim=4)
+    _check(kv, "kv", q.dtype, 5)
+    B, Sq, Hq, D = q.shape
+    Sk, two, Hkv = kv.shape[1], kv.shape[2], kv.shape[3]
+    if two != 2 or kv.shape[4] != D or kv.shape[0] != B:
+        raise ValueError("kv must be (B, Sk, 2, Hkv, D)")
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
+    lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = lib().fa_fwd_kvpacked(_ptr(q), _ptr(kv), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, _dt(q), scale,
+                               int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), _stream(stream))
+    _raise("fa_fwd_kvpacked", st)
+    return out, lse
+
+
+def fa_bwd_kvpacked(q, kv, out, dout, lse, dq=None, dkv=None, scale=None, causal=False, window=(-1, -1),
+                    softcap=0.0, alibi_slopes=None, deterministic=False, workspace=None, stream=None):
+    """Gradients (dq, dkv (B,Sk,2,Hkv,D)) of fa_fwd_kvpacked."""
+    _check(q, "q", ndim=4)
+    _check(kv, "kv", q.dtype, 5)
+    for n, t in (("out", out), ("dout", dout)):
+        _check(t, n, q.dtype, 4)
+    _check(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = kv.shape[1], kv.shape[3]
+    dq = torch.empty_like(q) if dq is None else _check(dq, "dq", q.dtype)
+    dkv = torch.empty_like(kv) if dkv is None else _check(dkv, "dkv", q.dtype)
+    L = lib()
+    ws_bytes = L.fa_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D, int(bool(deterministic)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_bwd_kvpacked(_ptr(q), _ptr(kv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dkv), B, Sq,
+                           Sk, Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes),
+                           int(bool(deterministic)), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise("fa_bwd_kvpacked", st)
+    return dq, dkv
 
 
 # --------------------------------------------------------------- varlen ----

@@ -45,7 +45,8 @@ struct BwdParams {
   const int* cu_q;
   const int* cu_k;
   int Sq, Sk, Hq, g, total_q;
-  int q_rstride, k_rstride;
+  // elements between consecutive tokens: q; k and v; o and dout; dq; dk and dv
+  int q_rstride, k_rstride, o_rstride, dq_rstride, dkv_rstride;
   float scale, scale_log2, scale_over_cap, cap_log2, inv_cap_log2;
   const float* alibi;
   int wl, wr;
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const bool ok = token < p.n_tokens;
   float acc = 0.0f;
   if (ok) {
-    const int64_t base = (int64_t)token * p.q_rstride + h * D + ch * 8;
+    const int64_t base = (int64_t)token * p.o_rstride + h * D + ch * 8;
     const u32x4 a = gload128(p.o + base);
     const u32x4 c = gload128(p.dout + base);
 #pragma unroll
@@ -203,8 +204,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
       const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * D;
+      const int64_t ooff = (int64_t)sb.q_start * p.o_rstride + (int64_t)hq * D;
       dma_tile<D, BR, NW>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
-      dma_tile<D, BR, NW>(st + TILE, p.dout + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW>(st + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
         const int i = min(i0 + lane, Sq - 1);
@@ -309,8 +311,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (key_ok) {
-    uint16_t* dkrow = p.dk + krow;
-    uint16_t* dvrow = p.dv + krow;
+    const int64_t drow_off = (int64_t)(sb.k_start + my_key) * p.dkv_rstride + hk * D;
+    uint16_t* dkrow = p.dk + drow_off;
+    uint16_t* dvrow = p.dv + drow_off;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -362,12 +365,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const bool row_ok = my_row < Sq;
   const int ip = my_row + off;
   const int64_t qrow = (int64_t)(sb.q_start + my_row) * p.q_rstride + h * D;
+  const int64_t orow = (int64_t)(sb.q_start + my_row) * p.o_rstride + h * D;
 
   u32x4 qreg[KC], doreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     qreg[c] = row_ok ? gload128(p.q + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
-    doreg[c] = row_ok ? gload128(p.dout + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    doreg[c] = row_ok ? gload128(p.dout + orow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
   float lse2 = INFINITY, dv_row = 0.0f;  // rows past the end: P = 0
   if (row_ok) {
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   }
 
   if (row_ok) {
-    uint16_t* drow = p.dq + qrow;
+    uint16_t* drow = p.dq + (int64_t)(sb.q_start + my_row) * p.dq_rstride + h * D;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -574,6 +578,9 @@ static void fill_common(BwdParams& p, const void* q, const void* k, const void* 
   p.g = Hq / Hkv;
   p.q_rstride = Hq * D;
   p.k_rstride = Hkv * D;
+  p.o_rstride = Hq * D;
+  p.dq_rstride = Hq * D;
+  p.dkv_rstride = Hkv * D;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
@@ -610,12 +617,19 @@ extern "C" size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int d
   return 2 * align_up((size_t)total_q * Hq * sizeof(float), 256);
 }
 
+// Row strides (elements between consecutive tokens) of q; k and v; dq;
+// dk and dv; 0 = contiguous.  out and dout are always contiguous.
+struct BwdStrides {
+  int q, kv, dq, dkv;
+};
+
 static int bwd_dense(const void* q, const void* k, const void* v, const void* out, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv,
                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
                      float scale, int causal, int window_left, int window_right, float softcap,
                      const float* alibi_slopes, const DropSpec& drop, int deterministic,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream,
+                     BwdStrides rs = BwdStrides{0, 0, 0, 0}) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
@@ -630,6 +644,10 @@ static int bwd_dense(const void* q, const void* k, const void* v, const void* ou
   p.Sq = Sq;
   p.Sk = Sk;
   p.drop = drop;
+  if (rs.q) p.q_rstride = rs.q;
+  if (rs.kv) p.k_rstride = rs.kv;
+  if (rs.dq) p.dq_rstride = rs.dq;
+  if (rs.dkv) p.dkv_rstride = rs.dkv;
   return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, B * Sq, causal, (hipStream_t)stream);
 }
 
@@ -684,6 +702,35 @@ extern "C" int fa_bwd_dropout(const void* q, const void* k, const void* v, const
   return bwd_dense(q, k, v, out, dout, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
                    window_left, window_right, softcap, alibi_slopes, drop, deterministic, workspace,
                    workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_qkvpacked(const void* qkv, const void* out, const void* dout, const float* lse,
+                                void* dqkv, int B, int S, int H, int D, int dtype,
+                                float scale, int causal, int window_left, int window_right, float softcap,
+                                const float* alibi_slopes, int deterministic,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!aligned16(qkv) || !aligned16(dqkv) || H < 1 || D < 1) return FA_ERR_INVALID_ARG;
+  const uint16_t* b = (const uint16_t*)qkv;
+  uint16_t* g = (uint16_t*)dqkv;
+  const int hd = H * D;
+  return bwd_dense(b, b + hd, b + 2 * hd, out, dout, lse, g, g + hd, g + 2 * hd, B, S, S, H, H, D, dtype,
+                   scale, causal, window_left, window_right, softcap, alibi_slopes, DropSpec{}, deterministic,
+                   workspace, workspace_bytes, stream, BwdStrides{3 * hd, 3 * hd, 3 * hd, 3 * hd});
+}
+
+extern "C" int fa_bwd_kvpacked(const void* q, const void* kv, const void* out, const void* dout,
+                               const float* lse, void* dq, void* dkv,
+                               int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                               float scale, int causal, int window_left, int window_right, float softcap,
+                               const float* alibi_slopes, int deterministic,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!aligned16(kv) || !aligned16(dkv) || Hkv < 1 || D < 1) return FA_ERR_INVALID_ARG;
+  const uint16_t* b = (const uint16_t*)kv;
+  uint16_t* g = (uint16_t*)dkv;
+  const int hd = Hkv * D;
+  return bwd_dense(q, b, b + hd, out, dout, lse, dq, g, g + hd, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
+                   window_left, window_right, softcap, alibi_slopes, DropSpec{}, deterministic, workspace,
+                   workspace_bytes, stream, BwdStrides{0, 2 * hd, 0, 2 * hd});
 }
 
 extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,

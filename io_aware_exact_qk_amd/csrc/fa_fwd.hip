@@ -38,8 +38,9 @@ struct FwdParams {
   int Sq, Sk;       // per-batch lengths (dense layout)
   int Hq, g;        // query heads, query heads per K/V head
   int total_q;      // packed layout: LSE row stride
-  int q_rstride;    // elements between consecutive tokens of q/o (Hq * D)
-  int k_rstride;    // elements between consecutive tokens of k/v (Hkv * D)
+  int q_rstride;    // elements between consecutive tokens of q (Hq * D unless packed)
+  int k_rstride;    // elements between consecutive tokens of k and of v (Hkv * D unless packed)
+  int o_rstride;    // elements between consecutive tokens of o (Hq * D)
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap
   float cap_log2;       // softcap * log2(e)
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const float l_tot = l_run + xor32(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) / l_tot : 0.0f;
-    uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.q_rstride + h * D;
+    uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.o_rstride + h * D;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -421,10 +422,17 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
   return launch_status();
 }
 
+// Row strides (elements between consecutive tokens) of q, of k and v, and
+// of out; 0 = the contiguous layout (Hq * D, Hkv * D, Hq * D).
+struct RowStrides {
+  int q, kv, o;
+};
+
 static int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse,
                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
                      float scale, int causal, int window_left, int window_right, float softcap,
-                     const float* alibi_slopes, const DropSpec& drop, void* stream) {
+                     const float* alibi_slopes, const DropSpec& drop, void* stream,
+                     RowStrides rs = RowStrides{0, 0, 0}) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
@@ -441,8 +449,9 @@ static int fwd_dense(const void* q, const void* k, const void* v, void* out, flo
   prm.Sk = Sk;
   prm.Hq = Hq;
   prm.g = Hq / Hkv;
-  prm.q_rstride = Hq * D;
-  prm.k_rstride = Hkv * D;
+  prm.q_rstride = rs.q ? rs.q : Hq * D;
+  prm.k_rstride = rs.kv ? rs.kv : Hkv * D;
+  prm.o_rstride = rs.o ? rs.o : Hq * D;
   prm.alibi = alibi_slopes;
   prm.wl = window_left;
   prm.wr = window_right;
@@ -477,6 +486,7 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
   prm.total_q = total_q;
   prm.q_rstride = Hq * D;
   prm.k_rstride = Hkv * D;
+  prm.o_rstride = Hq * D;
   prm.alibi = alibi_slopes;
   prm.wl = window_left;
   prm.wr = window_right;
@@ -505,6 +515,28 @@ extern "C" int fa_fwd_dropout(const void* q, const void* k, const void* v, void*
   if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
   return fwd_dense(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal, window_left,
                    window_right, softcap, alibi_slopes, drop, stream);
+}
+
+extern "C" int fa_fwd_qkvpacked(const void* qkv, void* out, float* lse, int B, int S, int H, int D,
+                                int dtype, float scale, int causal, int window_left, int window_right,
+                                float softcap, const float* alibi_slopes, void* stream) {
+  if (!aligned16(qkv) || H < 1 || D < 1) return FA_ERR_INVALID_ARG;
+  const uint16_t* base = (const uint16_t*)qkv;
+  const int hd = H * D;
+  return fwd_dense(base, base + hd, base + 2 * hd, out, lse, B, S, S, H, H, D, dtype, scale, causal,
+                   window_left, window_right, softcap, alibi_slopes, DropSpec{}, stream,
+                   RowStrides{3 * hd, 3 * hd, hd});
+}
+
+extern "C" int fa_fwd_kvpacked(const void* q, const void* kv, void* out, float* lse,
+                               int B, int Sq, int Sk, int Hq, int Hkv, int D, int dtype,
+                               float scale, int causal, int window_left, int window_right, float softcap,
+                               const float* alibi_slopes, void* stream) {
+  if (!aligned16(kv) || Hkv < 1 || D < 1) return FA_ERR_INVALID_ARG;
+  const uint16_t* base = (const uint16_t*)kv;
+  return fwd_dense(q, base, base + Hkv * D, out, lse, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
+                   window_left, window_right, softcap, alibi_slopes, DropSpec{}, stream,
+                   RowStrides{0, 2 * Hkv * D, 0});
 }
 
 extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
