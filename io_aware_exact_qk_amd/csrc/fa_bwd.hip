@@ -55,8 +55,14 @@ struct BwdParams {
   DropSpec drop; // DROP kernels only
 };
 
-// dK/dV work-group: this many waves of 32 keys each (two waves per SIMD).
-constexpr int DKDV_WAVES = 8;
+// dK/dV work-group: waves of 32 keys each (two waves per SIMD) and query
+// tile rows.  D = 256 runs 4 waves (one per SIMD: K 64, dK and dV 256
+// registers) and 32-row query tiles so V rows plus two stages fit in LDS.
+template <int D>
+struct DkdvShape {
+  static constexpr int NW = D >= 256 ? 4 : 8;
+  static constexpr int BR = D >= 256 ? 32 : 64;
+};
 
 struct SeqBounds {
   int q_start, Sq, k_start, Sk;
@@ -148,11 +154,12 @@ __device__ __forceinline__ float softcap_grad(float ds, float pv, float x, int i
 // delta) are copied into LDS by DMA, double buffered; the copy of tile n+1
 // runs under the matrix work of tile n.
 template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = DKDV_WAVES, BC = 32 * NW, BR = 64;
+__global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = DkdvShape<D>::NW, BC = 32 * NW, BR = DkdvShape<D>::BR;
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BR * D * 2;
-  constexpr int STAGE = 2 * TILE + 2 * BR * 4;
+  // LSE and delta rows: 64 floats each whatever BR is (one 4-byte DMA per lane)
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
   // V rows of the work-group's keys (B operand of dP = dO V^T), and two stage
   // buffers, distinct arrays so that reads of one are never ordered behind
   // the DMA into the other
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
         const int i = min(i0 + lane, Sq - 1);
-        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + 2 * TILE + w * BR * 4);
+        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + 2 * TILE + w * 64 * 4);
       }
     };
 
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       const char* qt = st;
       const char* dot = st + TILE;
       const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
-      const float* dvs = lse2 + BR;
+      const float* dvs = lse2 + 64;
       const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
       const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
 #pragma unroll
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 // work-groups per CU; K/V tiles of 64 keys are copied into LDS by DMA,
 // double buffered.
 template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BC * D * 2;
@@ -494,7 +501,8 @@ template <int D, int DT, bool SC, bool AL, bool DR>
 static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
   if (nwg_kv > 0) {
     prof_before(FA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR>), dim3(nwg_kv), dim3(64 * DKDV_WAVES), 0, st, dkdv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR>), dim3(nwg_kv), dim3(64 * DkdvShape<D>::NW), 0, st,
+                       dkdv);
     prof_after(FA_KERNEL_BWD_DKDV, st);
   }
   if (nwg_q > 0) {
@@ -537,7 +545,8 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   const long long pre_threads = (long long)n_tokens * base.Hq * (D / 8);
   const long long nwg_pre = (pre_threads + 255) / 256;
   BwdParams kv = base;
-  kv.n_tiles = (max_sk + 32 * DKDV_WAVES - 1) / (32 * DKDV_WAVES);
+  const int kv_keys = 32 * (D >= 256 ? DkdvShape<256>::NW : DkdvShape<128>::NW);
+  kv.n_tiles = (max_sk + kv_keys - 1) / kv_keys;
   kv.n_heads = Hkv;
   kv.n_batch = nbatch;
   kv.reverse = 0;
@@ -552,12 +561,25 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * nbatch;
   if (nwg_pre > 0x7fffffffLL || nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const bool sc = base.cap_log2 > 0.0f, al = base.alibi != nullptr;
-  if (D == 128) {
-    if (dtype == FA_DTYPE_BF16) launch_all<128, DT_BF16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
-    else launch_all<128, DT_F16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
-  } else {
-    if (dtype == FA_DTYPE_BF16) launch_all<64, DT_BF16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
-    else launch_all<64, DT_F16>(pre, (int)nwg_pre, kv, dq, (int)nwg_kv, (int)nwg_q, sc, al, st);
+  const bool bf = dtype == FA_DTYPE_BF16;
+  const int np = (int)nwg_pre, nk = (int)nwg_kv, nq = (int)nwg_q;
+  switch (D) {
+    case 32:
+      if (bf) launch_all<32, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      else launch_all<32, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      break;
+    case 64:
+      if (bf) launch_all<64, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      else launch_all<64, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      break;
+    case 128:
+      if (bf) launch_all<128, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      else launch_all<128, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      break;
+    default:
+      if (bf) launch_all<256, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      else launch_all<256, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      break;
   }
   return launch_status();
 }

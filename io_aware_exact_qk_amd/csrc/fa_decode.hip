@@ -565,6 +565,8 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   if (rotary_cos && (!aligned4(rotary_cos) || !aligned4(rotary_sin))) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
   if (Sq_new != 1) return FA_ERR_UNSUPPORTED;
+  // the four-stage K register ring does not fit D = 256; D = 32 is not built
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
   if (num_splits == 0) num_splits = auto_splits(B, Hkv, max_blocks_per_seq);
   const size_t need = fa_kvcache_workspace_size(B, Sq_new, Hq, D, num_splits);

@@ -105,15 +105,22 @@ __device__ __forceinline__ int frag_row(int i, int g) { return 8 * (i >> 2) + 4 
 //  * the 4 rows x 4 chunks of one half-wave transposed read (rows 4m..4m+3,
 //    chunks 4n..4n+3) land in 16 different slots.
 // D = 128 (16 chunks, one row per line): the low two row bits pick which
-// aligned group of 4 chunks, the next two permute inside it.  D = 64
+// aligned group of 4 chunks, the next two permute inside it.  D = 256 (32
+// chunks, two lines per row): the same permutation inside each line.  D = 64
 // (8 chunks, two rows per line, row parity picks the half line): row bit 1
-// picks the group of 4 chunks, row bits 2-3 permute inside it.
+// picks the group of 4 chunks, row bits 2-3 permute inside it.  D = 32
+// (4 chunks, four rows per line, the low two row bits pick the quarter
+// line): row bits 2-3 permute the 4 chunks.  In every case
+// swz(row + 8) = swz(row) ^ 2 and swz depends on row % 16 only.
 template <int D>
 __device__ __forceinline__ uint32_t swz(int row) {
-  if constexpr (D == 128) {
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
+  if constexpr (D >= 128) {
     return (uint32_t)(((row & 3) << 2) | ((row >> 2) & 3));
-  } else {
+  } else if constexpr (D == 64) {
     return (uint32_t)((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  } else {
+    return (uint32_t)((row >> 2) & 3);
   }
 }
 
@@ -263,12 +270,15 @@ template <int D, int ROWS, int NWAVES, bool FAST = true>
 __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64_t rstride, int row0,
                                          int nrows, int w, int lane) {
   constexpr int NCH = D / 8, RPB = 64 / NCH, NBLK = ROWS / RPB;
-  static_assert(NBLK % NWAVES == 0, "tile blocks must divide among the waves");
+  // more waves than 1 KB blocks (narrow tiles): the extra waves copy nothing
+  constexpr int PER = (NBLK + NWAVES - 1) / NWAVES;
+  static_assert(NBLK % NWAVES == 0 || NBLK < NWAVES, "tile blocks must divide among the waves");
+  if (NBLK < NWAVES && w >= NBLK) return;
   const int rin = lane / NCH, pch = lane % NCH;
   if (FAST && row0 + ROWS <= nrows) {
     const char* b0 = reinterpret_cast<const char*>(base + (int64_t)row0 * rstride);
 #pragma unroll
-    for (int i = 0; i < NBLK / NWAVES; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int blk = i * NWAVES + w;
       const int row = blk * RPB + rin;
       // re-derived per call: hoisting whole 64-bit addresses out of the tile
@@ -278,7 +288,7 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NBLK / NWAVES; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int blk = i * NWAVES + w;
       const int row = blk * RPB + rin;
       const int lch = pch ^ (int)swz<D>(row);

@@ -51,8 +51,10 @@ struct FwdParams {
   DropSpec drop;        // DROP kernels only
 };
 
+// D = 256 needs the whole register file of a SIMD (Q fragment 64, O
+// accumulator 128, two S tiles 64) and 128 KB of LDS: one wave per SIMD.
 template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16;               // MFMA steps along D
   constexpr int DB = D / 32;               // 32-wide output blocks along D
@@ -307,11 +309,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // Four distinct LDS arrays: K and V, double buffered, so reads of one are
     // never ordered behind the DMA into another.
     f32x16 sA[2], sB[2];
-    if constexpr (DROP) {
-      // With dropout the generator's integer work dominates the VALU, so the
-      // tiles run one after another (S, softmax, P V) with the next tile's
-      // K and V copied in underneath; this keeps the keep words in registers
-      // without spilling.
+    if constexpr (DROP || D >= 256) {
+      // With dropout the generator's integer work dominates the VALU, and at
+      // D = 256 two S tiles next to the O accumulator exceed the register
+      // file, so the tiles run one after another (S, softmax, P V) with the
+      // next tile's K and V copied in underneath.
       auto plain = [&](int t, const char* kt, const char* vt, char* kdst, char* vdst) {
         if (t + 1 < t_hi) {
           dma_k(t + 1, kdst);
@@ -411,12 +413,24 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const bool sc = softcap > 0.0f, al = prm.alibi != nullptr, dr = prm.drop.t > 0;
   prof_before(FA_KERNEL_FWD, st);
-  if (D == 128) {
-    if (dtype == FA_DTYPE_BF16) launch_fwd_d<128, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
-    else launch_fwd_d<128, DT_F16>(prm, sc, al, dr, (int)nwg, st);
-  } else {
-    if (dtype == FA_DTYPE_BF16) launch_fwd_d<64, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
-    else launch_fwd_d<64, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+  const bool bf = dtype == FA_DTYPE_BF16;
+  switch (D) {
+    case 32:
+      if (bf) launch_fwd_d<32, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+      else launch_fwd_d<32, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+      break;
+    case 64:
+      if (bf) launch_fwd_d<64, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+      else launch_fwd_d<64, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+      break;
+    case 128:
+      if (bf) launch_fwd_d<128, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+      else launch_fwd_d<128, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+      break;
+    default:
+      if (bf) launch_fwd_d<256, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
+      else launch_fwd_d<256, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+      break;
   }
   prof_after(FA_KERNEL_FWD, st);
   return launch_status();

@@ -54,3 +54,21 @@ def assert_grad(got, ref, what, mask=None):
     e = max_err(got, ref, mask)
     assert e <= TOL_GRAD * max(scale, 1e-30), f"{what}: max abs err {e:.3e} > {TOL_GRAD} * {scale:.3e}"
     return e
+
+
+def assert_out_rounded(got, ref, dtype, what="out"):
+    """Output tolerance plus half an ulp of the reference value in the output
+    dtype, per element.
+
+    Used where rows with one to a few visible keys (O close to a single v)
+    or dropout's 1/(1-p) scaling put |O| where rounding the result once to
+    16 bits, together with the 16-bit P operand of the PV product, already
+    reaches the plain tolerance: e.g. row 1 of a causal D = 256 bf16 case
+    gives 1.089e-2 both from the kernel and from the standard arithmetic
+    emulated on the CPU (float32 P rounded to bf16, output rounded once)."""
+    g, r = np64(got), np.asarray(ref, np.float64)
+    mant = 7 if dtype == torch.bfloat16 else 10
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - mant)
+    err = np.where(np.isinf(g) & np.isinf(r), 0.0, np.abs(g - r))
+    bad = ~(err <= TOL_OUT[dtype] + 0.5 * ulp)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond tolerance, max err {float(np.nanmax(err)):.3e}"
