@@ -162,6 +162,31 @@ def run_fwdbwd(args, torch, fa):
             fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
             drop.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
+    # other head dims at hidden 2048 (H = 2048 / D), S = 4K, B = 4
+    by_d = []
+    for Dh in (32, 64, 256):
+        Hh = 2048 // Dh
+        g = torch.Generator().manual_seed(2)
+        mk = lambda: torch.randn(4, 4096, Hh, Dh, generator=g).to(torch.bfloat16).to(dev)
+        q_, k_, v_, do_ = mk(), mk(), mk(), mk()
+        ws_ = torch.empty(fa.lib().fa_bwd_workspace_size(4, 4096, 4096, Hh, Hh, Dh, 0), device=dev,
+                          dtype=torch.uint8)
+        for causal in (False, True):
+            def one_d():
+                o_, l_ = fa.fa_fwd(q_, k_, v_, scale=1.0 / math.sqrt(Dh), causal=causal)
+                fa.fa_bwd(q_, k_, v_, o_, do_, l_, scale=1.0 / math.sqrt(Dh), causal=causal, workspace=ws_)
+            one_d()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                one_d()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 3
+            fl = 14 * Dh * visible_pairs(4, Hh, 4096, causal)
+            by_d.append({"D": Dh, "H": Hh, "S": 4096, "B": 4, "causal": causal, "ms": round(ms, 4),
+                         "tflops": round(fl / ms / 1e9, 1)})
+        del q_, k_, v_, do_, ws_
     # timed region
     fa.profiler_enable(4096)
     fa.profiler_reset()
@@ -193,7 +218,7 @@ def run_fwdbwd(args, torch, fa):
                 "traffic": recorded_traffic(dom),
                 "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
     return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
-                roofline=roofline, flops_step=flops_step, dropout=drop)
+                roofline=roofline, flops_step=flops_step, dropout=drop, by_head_dim=by_d)
 
 
 # ---------------------------------------------------------------------------
@@ -408,6 +433,7 @@ def main():
         "kernels": fb["kernels"],
         "per_config": fb["per_config"],
         "dropout_p0.1": fb["dropout"],
+        "head_dims_s4096": fb["by_head_dim"],
         "decode": dec,
     }
     print(json.dumps(line))
