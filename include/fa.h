@@ -220,7 +220,8 @@ int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const voi
  * Incremental decode against a (paged) KV cache (section "增量解码场景
  * flash_attn_with_kvcache"): the new k/v are appended to the cache in place
  * and the new queries attend over the cache plus the appended tokens.
- *   q (B, Sq_new, Hq, D) in; this build supports Sq_new == 1.
+ *   q (B, Sq_new, Hq, D) in; (Hq / Hkv) * Sq_new <= 32 (the new queries of
+ *     one K/V head are the 32 columns of one matrix tile), D in {64, 128}.
  *   k_new/v_new (B, Sq_new, Hkv, D) in, or both NULL (attend without append).
  *   k_cache/v_cache in/out: paged (n_pages, page_size, Hkv, D) when
  *     block_table != NULL, else contiguous (B, max_blocks_per_seq*page_size, Hkv, D).
@@ -239,13 +240,18 @@ int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const voi
  *     result does not depend on it beyond float32 rounding.  num_splits == 0:
  *     the library chooses (about 1024 work-groups over B * Hkv, at most 32
  *     splits and at most max_blocks_per_seq).
- *   causal: accepted; with Sq_new == 1 the new query sits at the last
- *     position (bottom-right alignment) and sees every earlier key.
- *   window_left (-1 = unbounded): keys before position
- *     cache_seqlens[b] + Sq_new - 1 - window_left are masked; window_right
- *     has no effect with Sq_new == 1.
+ *   Positions: with k_new the keys are the cache plus the Sq_new appended
+ *     rows; new query t sits at key position n_keys - Sq_new + t
+ *     (bottom-right alignment) and is rotated at cache_seqlens[b] + t.
+ *   causal: new query t sees the keys up to its own position (with
+ *     Sq_new == 1 that is every key); otherwise it sees every key.
+ *   window_left / window_right (-1 = unbounded): keys outside
+ *     [position - window_left, position + window_right] are masked (causal
+ *     sets window_right to 0).
  *   softcap (0 = off) and alibi_slopes (NULL or float32 (Hq,)): as in
- *     fa_fwd, with the ALiBi distance measured from the new query's position.
+ *     fa_fwd, with the ALiBi distance measured from each new query's position.
+ *   With Sq_new > 1 the append runs as its own kernel before the attention;
+ *   with Sq_new == 1 the attention kernel appends in its prologue.
  *   workspace: fa_kvcache_workspace_size(...) bytes (0 when num_splits == 1),
  *     computed with the same num_splits argument (0 included).
  * Appended slot (b, cache_seqlens[b] + t) receives the rotated k_new rounded

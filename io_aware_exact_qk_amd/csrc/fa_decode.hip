@@ -56,6 +56,9 @@ struct DecParams {
   float* ws_o;
   float* ws_lse;
   int B, Hq, Hkv, G, num_splits;
+  int T;       // new queries per sequence (Sq_new); G * T <= 32 columns
+  int causal;  // with T > 1: new query t sees keys up to its own position
+  int wr;      // right window (non-causal, T > 1), -1 = unbounded
   float scale_log2;
   // logit options (the OPTS kernels): softcap c (cap_log2 = c log2 e,
   // scale_over_cap = scale / c; 0 = off), ALiBi slopes per query head, and a
@@ -83,9 +86,13 @@ typedef __attribute__((address_space(4))) const int cint;  // constant address s
 // Batches up to this size are scheduled longest cache first.
 constexpr int kDecodeSortMax = 64;
 
-// OPTS: softcap, ALiBi or a left window is on.  The new query sits at
-// position n_keys - 1 (bottom-right alignment), sees every key at or before
-// it, and with a left window w only keys >= n_keys - 1 - w.
+// The G * T new queries of a K/V head are the MFMA columns (column
+// t * G + g = query head g of the group, new token t).  New token t sits at
+// position n_keys - T + t (bottom-right alignment); causal limits it to the
+// keys at or before that position (with T = 1 that is every key), a left
+// window w to keys >= position - w.  OPTS: softcap, ALiBi or a window is on.
+// With T > 1 the appended rows were written by decode_append_kernel before
+// this kernel starts; with T = 1 the kernel appends in its own prologue.
 template <int D, int DT, bool OPTS>
 __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int BK = 32;  // keys per wave tile
@@ -100,8 +107,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   __shared__ __attribute__((aligned(1024))) char vs3[4 * VT];
   __shared__ float mbuf[4 * 32], lbuf[4 * 32];
   __shared__ __attribute__((aligned(16))) char apbuf[4 * D];  // rotated k_new row, v_new row
-  __shared__ __attribute__((aligned(16))) char qst[33 * D * 2];  // query rows (G <= 32), k_new row
-  __shared__ float rot_cs[D];                                     // cos, sin at position L
+  __shared__ __attribute__((aligned(16))) char qst[33 * D * 2];  // query rows (G * T <= 32), k_new row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -136,12 +142,15 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   // does not have to drain.
   b = __builtin_amdgcn_readfirstlane(b);
   const int L = ((const cint*)p.cache_seqlens)[b];
+  const int T = p.T, G = p.G;
   const bool append = p.k_new != nullptr;
-  const int n_keys = L + (append ? 1 : 0);
+  const bool fused = append && T == 1;  // append in this kernel's prologue
+  const int n_keys = L + (append ? T : 0);
+  const int qpos0 = n_keys - T;  // position of new token 0
   const int page = p.page_size;
   const int n_pages = (n_keys + page - 1) / page;
-  // first visible key; the splits share the pages from its page on
-  const int key_lo = (OPTS && p.wl >= 0) ? max(0, n_keys - 1 - p.wl) : 0;
+  // first key any column sees; the splits share the pages from its page on
+  const int key_lo = (OPTS && p.wl >= 0) ? max(0, qpos0 - p.wl) : 0;
   const int pg0 = key_lo / page;
   const int per = (n_pages - pg0 + p.num_splits - 1) / p.num_splits;
   const int p_lo = pg0 + s_id * per;
@@ -149,32 +158,29 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   const int k_lo = max(p_lo * page, key_lo);
   const int k_hi = min(p_hi * page, n_keys);
 
-  // ---- stage the group's query rows, the k_new row and the rotary row of
-  // position L in LDS with independent loads (one round trip) ----
+  // ---- stage the query rows of the G * T columns and (T = 1 append) the
+  // k_new row in LDS with independent loads (one round trip) ----
   constexpr int NCH = D / 8;
   const int hr = p.cos ? p.rotary_dim / 2 : 0;  // rotary half width (0 = off)
   {
-    const int nq = p.G * NCH, nk = append ? NCH : 0;
-    const int total = nq + nk + 2 * hr;
-    for (int i = tid; i < total; i += 256) {
+    const int nq = G * T * NCH, nk = fused ? NCH : 0;
+    for (int i = tid; i < nq + nk; i += 256) {
       if (i < nq) {
-        const int row = i / NCH, ch = i % NCH;
-        const u32x4 v = gload128(p.q + ((int64_t)b * p.Hq + hkv * p.G + row) * D + ch * 8);
+        const int row = i / NCH, ch = i % NCH;  // row = column t * G + g
+        const int t = row / G, gq = row % G;
+        const u32x4 v = gload128(p.q + (((int64_t)b * T + t) * p.Hq + hkv * G + gq) * D + ch * 8);
         lds_write128(qst, (row * D + ch * 8) * 2, v);
-      } else if (i < nq + nk) {
+      } else {
         const int ch = i - nq;
         const u32x4 v = gload128(p.k_new + ((int64_t)b * p.Hkv + hkv) * D + ch * 8);
         lds_write128(qst, (32 * D + ch * 8) * 2, v);
-      } else {
-        const int j = i - nq - nk;  // cos[0..hr) then sin[0..hr) at position L
-        rot_cs[j] = j < hr ? p.cos[(int64_t)L * hr + j] : p.sin[(int64_t)L * hr + (j - hr)];
       }
     }
     __syncthreads();
   }
-  // Chunk ch (8 elements) of a staged row, rotated at position L: the
+  // Chunk ch (8 elements) of a staged row, rotated at position pos: the
   // half-split pairs (x_i, x_{i+hr}) for i < hr; dims >= 2 hr pass through.
-  auto rot8 = [&](const char* row, int ch, float x[8]) {
+  auto rot8 = [&](const char* row, int ch, int pos, float x[8]) {
     const u32x4 a = lds_read128(row, ch * 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -187,23 +193,31 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
       const int pch = first ? ch + hr / 8 : ch - hr / 8;
       const int fi0 = first ? d0 : d0 - hr;
       const u32x4 bv = lds_read128(row, pch * 16);
+      const float* cr = p.cos + (int64_t)pos * hr + fi0;
+      const float* sr = p.sin + (int64_t)pos * hr + fi0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float y = (e & 1) ? hi16<DT>(bv[e >> 1]) : lo16<DT>(bv[e >> 1]);
-        const float c = rot_cs[fi0 + e], sn = rot_cs[hr + fi0 + e];
+        const float c = cr[e], sn = sr[e];
         x[e] = first ? (x[e] * c - y * sn) : (x[e] * c + y * sn);
       }
     }
   };
 
-  // ---- query fragment (B operand, column = query head of the group) ----
-  const bool col_ok = r < p.G;
+  // ---- query fragment (B operand, column = new token t, query head g) ----
+  const bool col_ok = r < G * T;
+  const int col_t = col_ok ? r / G : 0;
+  const int qpos = qpos0 + col_t;                   // this column's query position
+  // last key it sees (a right bound only binds with T > 1)
+  const int right = p.causal ? 0 : p.wr;
+  const int last_key = right >= 0 ? min(n_keys - 1, qpos + right) : n_keys - 1;
+  const int first_key = (OPTS && p.wl >= 0) ? max(0, qpos - p.wl) : 0;
   u32x4 qhi[KC], qlo[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     if (col_ok) {
       float x[8], rem[8];
-      rot8(qst + r * (D * 2), 2 * c + hf, x);
+      rot8(qst + r * (D * 2), 2 * c + hf, L + col_t, x);
       qhi[c] = pack8<DT>(x);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
-  const float slope_log2 = (OPTS && p.alibi && col_ok) ? p.alibi[hkv * p.G + r] * kLog2e : 0.0f;
+  const float slope_log2 = (OPTS && p.alibi && col_ok) ? p.alibi[hkv * G + r % G] * kLog2e : 0.0f;
 
   // Element offset of the first row of the 32-key tile starting at key j0
   // (a tile never crosses a page: page_size is a multiple of 32).  Rows of
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   // One tile: `ka` / `vt` hold K and V of tile t.
   auto compute = [&](int t, u32x4 (&ka)[KC], char* vt) {
     const int j0 = t * BK;
-    if (append && L >= j0 && L < j0 + BK) {
+    if (fused && L >= j0 && L < j0 + BK) {
       // This tile holds the appended position: its row takes the rotated
       // k_new and v_new parked in LDS by the prologue instead of the stale
       // cache row that was streamed in.
@@ -280,15 +294,19 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float x = p.cap_log2 > 0.0f ? p.cap_log2 * tanh_exp(s[i] * p.scale_over_cap) : s[i] * p.scale_log2;
-        if (p.alibi) x -= slope_log2 * (float)(n_keys - 1 - (j0 + frag_row(i, hf)));
+        if (p.alibi) x -= slope_log2 * (float)abs(qpos - (j0 + frag_row(i, hf)));
         s[i] = x;
       }
     }
-    if (j0 + BK > n_keys || (OPTS && j0 < key_lo)) {
+    // keys past a column's own position (causal, T > 1), past the cache end,
+    // or left of its window are masked
+    const int min_last = right >= 0 ? min(n_keys - 1, qpos0 + right) : n_keys - 1;
+    const int max_first = (OPTS && p.wl >= 0) ? qpos0 + T - 1 - p.wl : 0;
+    if (j0 + BK - 1 > min_last || (OPTS && j0 < max_first)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int j = j0 + frag_row(i, hf);
-        s[i] = (j < n_keys && j >= key_lo) ? s[i] : -INFINITY;
+        s[i] = (j <= last_key && j >= first_key) ? s[i] : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   // k_new, writes the rotated key and v_new to the cache slot (no other
   // wave or work-group reads that slot) and parks both rows in LDS for the
   // tile that uses them.
-  if (append && L >= k_lo && L < k_hi && ((L / BK - t_lo) & 3) == w && r == L % BK) {
+  if (fused && L >= k_lo && L < k_hi && ((L / BK - t_lo) & 3) == w && r == L % BK) {
     const uint16_t* vnr = p.v_new + ((int64_t)b * p.Hkv + hkv) * D;
     const int64_t slot = tile_base(L - L % BK) + (int64_t)r * kvstride;
     u32x4 vv[KC];
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       float x[8];
-      rot8(qst + 32 * (D * 2), 2 * c + hf, x);
+      rot8(qst + 32 * (D * 2), 2 * c + hf, L, x);
       const u32x4 kk = pack8<DT>(x);
       gstore128(p.k_cache + slot + (2 * c + hf) * 8, kk);
       gstore128(p.v_cache + slot + (2 * c + hf) * 8, vv[c]);
@@ -402,9 +420,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     __syncthreads();
   }
   // ---- write: each thread handles (column, d) pairs ----
-  for (int idx = tid; idx < p.G * D; idx += 256) {
+  for (int idx = tid; idx < G * T * D; idx += 256) {
     const int col = idx / D, d = idx % D;
-    const int h = hkv * p.G + col;
+    const int h = hkv * G + col % G, tt = col / G;
+    const int64_t bht = ((int64_t)b * p.Hq + h) * T + tt;  // (b, h, t) of lse and partials
     float Mc = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) Mc = fmaxf(Mc, mbuf[ww * 32 + col]);
@@ -417,12 +436,12 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     }
     const float o = lc > 0.0f ? obuf[d * 32 + col] / lc : 0.0f;
     if (p.num_splits == 1) {
-      uint16_t* orow = p.out + ((int64_t)b * p.Hq + h) * D;
+      uint16_t* orow = p.out + (((int64_t)b * T + tt) * p.Hq + h) * D;
       const uint32_t pk = pack2<DT>(o, 0.0f);
       orow[d] = (uint16_t)(pk & 0xffff);
-      if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = lc > 0.0f ? (Mc + fast_log2(lc)) * kLn2 : INFINITY;
+      if (d == 0 && p.lse) p.lse[bht] = lc > 0.0f ? (Mc + fast_log2(lc)) * kLn2 : INFINITY;
     } else {
-      const int64_t pi = ((int64_t)b * p.Hq + h) * p.num_splits + s_id;
+      const int64_t pi = bht * p.num_splits + s_id;
       p.ws_o[pi * D + d] = o;
       if (d == 0) p.ws_lse[pi] = lc > 0.0f ? (Mc + fast_log2(lc)) * kLn2 : -INFINITY;
     }
@@ -436,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
 // with the partial loads unrolled so several are in flight.
 template <int D, int DT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecParams p) {
-  const int bh = blockIdx.x;  // b * Hq + h
+  const int bh = blockIdx.x;  // (b * Hq + h) * T + t
   const int lane = threadIdx.x;
   const int S = p.num_splits;
   const float* ls = p.ws_lse + (int64_t)bh * S;
@@ -487,28 +506,82 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecParams p) {
       }
     }
   }
+  // out is (B, T, Hq, D); bh = (b * Hq + h) * T + t
+  const int tt = bh % p.T, h = (bh / p.T) % p.Hq, b = bh / (p.T * p.Hq);
+  uint16_t* orow = p.out + (((int64_t)b * p.T + tt) * p.Hq + h) * D;
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
     const int d = lane + 64 * k;
     if (d < D) {
       const uint32_t pk = pack2<DT>(o[k], 0.0f);
-      p.out[(int64_t)bh * D + d] = (uint16_t)(pk & 0xffff);
+      orow[d] = (uint16_t)(pk & 0xffff);
     }
   }
   if (lane == 0 && p.lse) p.lse[bh] = L;
+}
+
+// Append for T > 1 new tokens, launched before the split kernel: one wave
+// per (sequence, new token, K/V head) rotates k_new at position
+// cache_seqlens[b] + t (half-split pairs, caller's tables), rounds it once to
+// the cache dtype and writes it and v_new to the token's cache slot.  The
+// split kernel then reads the slots like any other cache row.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void decode_append_kernel(DecParams p) {
+  constexpr int NCH = D / 8;
+  const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (id >= p.B * p.T * p.Hkv || lane >= NCH) return;
+  const int hkv = id % p.Hkv, t = (id / p.Hkv) % p.T, b = id / (p.Hkv * p.T);
+  const int pos = p.cache_seqlens[b] + t;
+  int64_t slot;
+  if (p.block_table) {
+    const int phys = p.block_table[(int64_t)b * p.max_blocks + pos / p.page_size];
+    slot = (((int64_t)phys * p.page_size + pos % p.page_size) * p.Hkv + hkv) * D;
+  } else {
+    slot = (((int64_t)b * p.max_blocks * p.page_size + pos) * p.Hkv + hkv) * D;
+  }
+  const int64_t src = (((int64_t)b * p.T + t) * p.Hkv + hkv) * D;
+  const int ch = lane, d0 = 8 * ch;
+  const int hr = p.cos ? p.rotary_dim / 2 : 0;
+  const u32x4 a = gload128(p.k_new + src + d0);
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = lo16<DT>(a[e]);
+    x[2 * e + 1] = hi16<DT>(a[e]);
+  }
+  if (d0 < 2 * hr) {
+    const bool first = d0 < hr;
+    const int pd = first ? d0 + hr : d0 - hr;  // partner chunk
+    const int fi0 = first ? d0 : d0 - hr;
+    const u32x4 bv = gload128(p.k_new + src + pd);
+    const float* cr = p.cos + (int64_t)pos * hr + fi0;
+    const float* sr = p.sin + (int64_t)pos * hr + fi0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = (e & 1) ? hi16<DT>(bv[e >> 1]) : lo16<DT>(bv[e >> 1]);
+      x[e] = first ? (x[e] * cr[e] - y * sr[e]) : (x[e] * cr[e] + y * sr[e]);
+    }
+  }
+  gstore128(p.k_cache + slot + d0, pack8<DT>(x));
+  gstore128(p.v_cache + slot + d0, gload128(p.v_new + src + d0));
 }
 
 template <int D, int DT>
 static int launch_decode(const DecParams& p, bool opts, hipStream_t st) {
   const long long nwg = (long long)p.B * p.Hkv * p.num_splits;
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (p.k_new && p.T > 1) {
+    const long long rows = (long long)p.B * p.T * p.Hkv;
+    hipLaunchKernelGGL((decode_append_kernel<D, DT>), dim3((int)((rows + 3) / 4)), dim3(256), 0, st, p);
+  }
   prof_before(FA_KERNEL_DECODE_SPLIT, st);
   if (opts) hipLaunchKernelGGL((decode_split_kernel<D, DT, true>), dim3((int)nwg), dim3(256), 0, st, p);
   else hipLaunchKernelGGL((decode_split_kernel<D, DT, false>), dim3((int)nwg), dim3(256), 0, st, p);
   prof_after(FA_KERNEL_DECODE_SPLIT, st);
   if (p.num_splits > 1) {
     prof_before(FA_KERNEL_DECODE_COMBINE, st);
-    hipLaunchKernelGGL((decode_combine_kernel<D, DT>), dim3(p.B * p.Hq), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_combine_kernel<D, DT>), dim3(p.B * p.Hq * p.T), dim3(64), 0, st, p);
     prof_after(FA_KERNEL_DECODE_COMBINE, st);
   }
   return launch_status();
@@ -549,7 +622,6 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
                               float scale, int causal, int window_left, int window_right, float softcap,
                               const float* alibi_slopes, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  (void)causal;
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (B < 1 || Sq_new < 1 || num_splits < 0 || max_blocks_per_seq < 1) return FA_ERR_INVALID_ARG;
@@ -564,10 +636,10 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   if (rotary_cos && (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > D)) return FA_ERR_INVALID_ARG;
   if (rotary_cos && (!aligned4(rotary_cos) || !aligned4(rotary_sin))) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
-  if (Sq_new != 1) return FA_ERR_UNSUPPORTED;
   // the four-stage K register ring does not fit D = 256; D = 32 is not built
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  // the G * Sq_new new queries of a K/V head are the 32 MFMA columns
+  if ((long long)(Hq / Hkv) * Sq_new > 32) return FA_ERR_UNSUPPORTED;
   if (num_splits == 0) num_splits = auto_splits(B, Hkv, max_blocks_per_seq);
   const size_t need = fa_kvcache_workspace_size(B, Sq_new, Hq, D, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
@@ -595,6 +667,9 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
   p.num_splits = num_splits;
+  p.T = Sq_new;
+  p.causal = causal ? 1 : 0;
+  p.wr = window_right;
   p.scale_log2 = scale * kLog2e;
   p.cap_log2 = softcap * kLog2e;
   p.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;

@@ -32,6 +32,11 @@ def _oracle(c, append=True, **opts):
                        cache_dtype="bf16" if c.q.dtype == torch.bfloat16 else "fp16", **opts)
 
 
+def _masked_lse_ok(lse, ref):
+    """LSE check that treats empty rows (+inf on both sides) as equal."""
+    assert_lse(lse, ref)
+
+
 def _check_cache(c, ref, kc, vc, paged=True):
     """Appended slots hold the oracle's k_app (within 1 ulp when rotated) and
     v_new exactly; every other cache byte is unchanged."""
@@ -192,3 +197,37 @@ def test_auto_splits(B, Hkv, lens):
     assert_out(out, ref["out"], c.q.dtype)
     assert_lse(lse, ref["lse"])
     _check_cache(c, ref, kc, vc)
+
+
+# Several new tokens per sequence (chunked append): G * T <= 32 columns.
+MULTI = [
+    # B, Hq, Hkv, D, page, seqlens, T, causal, append, paged, rotary, opts, splits
+    (3, 8, 2, 128, 64, [300, 62, 1], 4, True, True, True, 64, {}, 1),
+    (3, 8, 2, 128, 64, [300, 62, 1], 4, True, True, True, 64, {}, 3),
+    (2, 4, 4, 64, 32, [31, 200], 8, True, True, False, 32, {}, 2),
+    (2, 8, 1, 128, 128, [500, 129], 4, False, True, True, 0, {}, 4),
+    (2, 4, 2, 128, 64, [190, 70], 16, True, False, True, 0, {}, 2),
+    (2, 8, 2, 128, 64, [400, 90], 3, True, True, True, 64,
+     dict(window=(50, -1), softcap=20.0, alibi=True), 3),
+    (1, 2, 1, 128, 32, [5], 16, True, True, True, 0, {}, 1),
+    (2, 4, 2, 64, 64, [150, 300], 6, False, True, True, 0, dict(window=(40, 3)), 2),
+]
+
+
+@pytest.mark.parametrize("case", MULTI, ids=[f"m{i}" for i in range(len(MULTI))])
+def test_multi_token_decode(case):
+    B, Hq, Hkv, D, page, lens, T, causal, append, paged, rd, opts, splits = case
+    c = decode_case(B=B, Hq=Hq, Hkv=Hkv, D=D, page=page, seqlens=lens, seed=59 + T, rotary_dim=rd,
+                    paged=paged, sq_new=T)
+    slopes = alibi_slopes(Hq) if opts.get("alibi") else None
+    kw = dict(window=opts.get("window", (-1, -1)), softcap=opts.get("softcap", 0.0))
+    say("decode multi-token", case)
+    out, lse, kc, vc = _run(c, splits, append=append, causal=causal,
+                            alibi_slopes=None if slopes is None else slopes.to(DEV), **kw)
+    ref = _oracle(c, append=append, causal=causal, alibi_slopes=slopes, **kw)
+    assert_out(out, ref["out"], c.q.dtype)
+    _masked_lse_ok(lse, ref["lse"])
+    if append:
+        _check_cache(c, ref, kc, vc)
+    else:
+        assert torch.equal(kc.cpu(), c.k_cache) and torch.equal(vc.cpu(), c.v_cache)

@@ -108,7 +108,7 @@ def test_kvcache_rejects(lib):
     assert call(cos=F, sin=F, rd=256) == 1
     assert call(knew=None) == 1
     assert call(splits=-1) == 1
-    assert call(Sq=2) == 2
+    assert call(Sq=2, Hq=32, Hkv=1) == 2  # 32 query heads x 2 new tokens > 32 MFMA columns
     assert call(Hq=66, Hkv=1) == 2
     assert call(splits=4) == 3  # needs a workspace
     assert call(splits=0) == 3  # the automatic count here is 4: needs a workspace

@@ -184,11 +184,11 @@ class DecodeCase:
 
 def decode_case(B=8, Hq=32, Hkv=8, D=128, page=256, seqlens=None, lo=1024, hi=65536,
                 seed=5, dtype="bf16", rotary_dim=None, paged=True, poison=1.0e4,
-                max_pos=None, name="") -> DecodeCase:
-    """Decode inputs.  Sequence b owns ceil((L_b+1)/page) pages (room for the
-    appended token); pages come from a seeded permutation of the pool and are
-    handed to the sequences in order.  Slots past L_b are filled with +/-poison
-    so that any read of them shows up in the output."""
+                max_pos=None, name="", sq_new=1) -> DecodeCase:
+    """Decode inputs.  Sequence b owns ceil((L_b+sq_new)/page) pages (room for
+    the appended tokens); pages come from a seeded permutation of the pool and
+    are handed to the sequences in order.  Slots past L_b are filled with
+    +/-poison so that any read of them shows up in the output."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     rng = np.random.default_rng(seed)
     if seqlens is None:
@@ -196,7 +196,7 @@ def decode_case(B=8, Hq=32, Hkv=8, D=128, page=256, seqlens=None, lo=1024, hi=65
     else:
         L = np.asarray(seqlens, dtype=np.int64)
     L = L.astype(np.int64)
-    need = [(int(x) + 1 + page - 1) // page for x in L]
+    need = [(int(x) + sq_new + page - 1) // page for x in L]
     n_pages = int(sum(need))
     perm = rng.permutation(n_pages)
     max_blocks = max(need) if seqlens is not None else (hi + 1 + page - 1) // page
@@ -214,9 +214,9 @@ def decode_case(B=8, Hq=32, Hkv=8, D=128, page=256, seqlens=None, lo=1024, hi=65
         cap = max_blocks * page
         k_cache = randn(g, (B, cap, Hkv, D), dt)
         v_cache = randn(g, (B, cap, Hkv, D), dt)
-    q = randn(g, (B, 1, Hq, D), dt)
-    k_new = randn(g, (B, 1, Hkv, D), dt)
-    v_new = randn(g, (B, 1, Hkv, D), dt)
+    q = randn(g, (B, sq_new, Hq, D), dt)
+    k_new = randn(g, (B, sq_new, Hkv, D), dt)
+    v_new = randn(g, (B, sq_new, Hkv, D), dt)
     # poison every slot at or past L_b (slot L_b is overwritten by the append)
     sign = torch.where(torch.arange(D) % 2 == 0, 1.0, -1.0).to(dt) * poison
     for b in range(B):
@@ -230,7 +230,7 @@ def decode_case(B=8, Hq=32, Hkv=8, D=128, page=256, seqlens=None, lo=1024, hi=65
                 v_cache[b, j] = sign
     rd = D if rotary_dim is None else rotary_dim
     if rd > 0:
-        mp = int(L.max()) + 2 if max_pos is None else max_pos
+        mp = int(L.max()) + sq_new + 1 if max_pos is None else max_pos
         cos, sin = rotary_tables(mp, rd)
     else:
         cos = sin = None
