@@ -187,6 +187,40 @@ def run_fwdbwd(args, torch, fa):
             by_d.append({"D": Dh, "H": Hh, "S": 4096, "B": 4, "causal": causal, "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
         del q_, k_, v_, do_, ws_
+    # forward only: bf16 vs fp8 (q/k/v e4m3 with per-(batch, head) factors;
+    # the fp8 -> bf16 copy of V is inside the timed call)
+    fp8 = []
+    for t in cases:
+        if t["S"] < 4096:
+            continue
+        amax = lambda x: (x.float().abs().amax(dim=(1, 3)) / 240.0).contiguous()  # (B, H)
+        f8 = {}
+        for name in ("q", "k", "v"):
+            ds = amax(t[name])
+            f8[name] = (t[name].float() / ds[:, None, :, None]).to(torch.float8_e4m3fn)
+            f8["d" + name] = ds
+        ws8 = torch.empty(fa.lib().fa_fwd_fp8_workspace_size(t["B"], t["S"], H, D), device=dev, dtype=torch.uint8)
+        for causal in (False, True):
+            res = {"S": t["S"], "B": t["B"], "causal": causal}
+            for kind in ("bf16", "fp8"):
+                def one_f():
+                    if kind == "bf16":
+                        fa.fa_fwd(t["q"], t["k"], t["v"], out=t["out"], lse=t["lse"], scale=scale, causal=causal)
+                    else:
+                        fa.fa_fwd_fp8(f8["q"], f8["k"], f8["v"], f8["dq"], f8["dk"], f8["dv"], out=t["out"],
+                                      lse=t["lse"], scale=scale, causal=causal, workspace=ws8)
+                one_f()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(5):
+                    one_f()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 5
+                res[kind + "_ms"] = round(ms, 4)
+                res[kind + "_tflops"] = round(4 * D * visible_pairs(t["B"], H, t["S"], causal) / ms / 1e9, 1)
+            fp8.append(res)
+        del f8, ws8
     # timed region
     fa.profiler_enable(4096)
     fa.profiler_reset()
@@ -218,7 +252,7 @@ def run_fwdbwd(args, torch, fa):
                 "traffic": recorded_traffic(dom),
                 "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
     return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
-                roofline=roofline, flops_step=flops_step, dropout=drop, by_head_dim=by_d)
+                roofline=roofline, flops_step=flops_step, dropout=drop, by_head_dim=by_d, fp8=fp8)
 
 
 # ---------------------------------------------------------------------------
@@ -434,6 +468,7 @@ def main():
         "per_config": fb["per_config"],
         "dropout_p0.1": fb["dropout"],
         "head_dims_s4096": fb["by_head_dim"],
+        "fwd_bf16_vs_fp8": fb["fp8"],
         "decode": dec,
     }
     print(json.dumps(line))

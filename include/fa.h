@@ -164,6 +164,29 @@ int fa_bwd_kvpacked(const void* q, const void* kv, const void* out, const void* 
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 forward (page "FlashAttention实战指南：如何在AMD GPU上突破大模型训练瓶颈",
+ * section "性能优化技巧", item "FP8混合精度支持": FP8 support on AMD GPUs for
+ * lower memory bandwidth at kept accuracy; page "FlashAttention 实战指南…",
+ * section "版本怎么选": an FP8 forward pass).  q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D): OCP
+ * e4m3 bytes (torch.float8_e4m3fn); descale_q / descale_k / descale_v:
+ * NULL or float32 (B, Hkv) device arrays, the factor that turns the stored
+ * fp8 value of batch entry b, K/V head h (for q: its query heads) back into
+ * the real value.  out (B,Sq,Hq,D) bfloat16; lse as fa_fwd.  The result is
+ * attention on the dequantised inputs: S = q.k is formed exactly from the
+ * fp8 products on the fp8 matrix instruction and scaled by
+ * descale_q * descale_k; P V runs in bfloat16 after an exact fp8 -> bfloat16
+ * copy of v into the workspace, and O is scaled by descale_v.  D in {64, 128};
+ * options as fa_fwd.  workspace: fa_fwd_fp8_workspace_size(...) bytes.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Sq, int Sk, int Hq, int Hkv, int D,
+               float scale, int causal, int window_left, int window_right, float softcap,
+               const float* alibi_slopes, const float* descale_q, const float* descale_k,
+               const float* descale_v, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t fa_fwd_fp8_workspace_size(int B, int Sk, int Hkv, int D);
+
+/*
  * Dropout on the attention weights (the dropout_p argument of the attention
  * call in section "上手 FlashAttention 的三步走" and in the interface listing
  * of page "终极指南：如何通过FlashAttention实现Transformer模型的4倍加速与20倍内存优化").

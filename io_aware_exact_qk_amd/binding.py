@@ -80,6 +80,11 @@ def lib():
     L.fa_bwd_kvpacked.restype = _I
     L.fa_bwd_kvpacked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                                   _F, _P, _I, _P, _Z, _P]
+    L.fa_fwd_fp8.restype = _I
+    L.fa_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _P, _P, _P,
+                             _P, _Z, _P]
+    L.fa_fwd_fp8_workspace_size.restype = _Z
+    L.fa_fwd_fp8_workspace_size.argtypes = [_I] * 4
     L.fa_bwd_varlen_dropout.restype = _I
     L.fa_bwd_varlen_dropout.argtypes = L.fa_bwd_varlen.argtypes[:26] + _D + L.fa_bwd_varlen.argtypes[26:]
     L.fa_fwd_kvcache.restype = _I
@@ -286,6 +291,37 @@ def fa_bwd_kvpacked(q, kv, out, dout, lse, dq=None, dkv=None, scale=None, causal
                            workspace.numel() * workspace.element_size(), _stream(stream))
     _raise("fa_bwd_kvpacked", st)
     return dq, dkv
+
+
+# ------------------------------------------------------------------ fp8 ----
+def fa_fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, out=None, lse=None, scale=None,
+               causal=False, window=(-1, -1), softcap=0.0, alibi_slopes=None, workspace=None, stream=None):
+    """fp8 (torch.float8_e4m3fn) q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D) with float32
+    dequantisation factors (B, Hkv) each (None = 1) -> (out bf16, lse)."""
+    f8 = torch.float8_e4m3fn
+    _check(q, "q", f8, 4)
+    _check(k, "k", f8, 4)
+    _check(v, "v", f8, 4)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    for n, d in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        if d is not None:
+            _check(d, n, torch.float32, 2)
+            if tuple(d.shape) != (B, Hkv):
+                raise ValueError(f"{n} must be (B, Hkv)")
+    out = torch.empty(B, Sq, Hq, D, device=q.device, dtype=torch.bfloat16) if out is None else _check(out, "out", torch.bfloat16)
+    lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
+    L = lib()
+    ws_bytes = L.fa_fwd_fp8_workspace_size(B, Sk, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    st = L.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, scale,
+                      int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), _ptr(descale_q), _ptr(descale_k),
+                      _ptr(descale_v), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                      _stream(stream))
+    _raise("fa_fwd_fp8", st)
+    return out, lse
 
 
 # --------------------------------------------------------------- varlen ----

@@ -36,6 +36,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
@@ -46,6 +47,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 
 // ---------------------------------------------------------------- MFMA ----
+// 32 x 32 x 64 product of fp8 (OCP e4m3) operands, float32 accumulate: each
+// lane holds 32 contraction elements of its row (A) or column (B) as bytes;
+// the hardware pairs byte j of A lane (i, half g) with byte j of B lane
+// (n, half g), so any assignment of contraction indices to (g, j) that A and
+// B share gives the same product.  Zero block scales select the unscaled
+// instruction.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (DT == DT_BF16) {

@@ -49,11 +49,20 @@ struct FwdParams {
   int n_qtiles, n_heads, n_batch;
   int reverse;          // causal: heaviest tiles first
   DropSpec drop;        // DROP kernels only
+  // FP8 kernels: q and k are OCP e4m3 bytes, v the bfloat16 copy of the fp8
+  // values; per-(batch, K/V head) dequantisation factors, NULL = 1
+  const float* dsc_q;
+  const float* dsc_k;
+  const float* dsc_v;
 };
 
 // D = 256 needs the whole register file of a SIMD (Q fragment 64, O
 // accumulator 128, two S tiles 64) and 128 KB of LDS: one wave per SIMD.
-template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
+// FP8: S = K Q^T runs on the fp8 matrix instruction (32 x 32 x 64) from
+// fp8 Q fragments and fp8 K tiles; P V stays in bfloat16 (V converted
+// exactly beforehand), so only the logits change precision and they are
+// exact products of the fp8 inputs.
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP, bool FP8 = false>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16;               // MFMA steps along D
@@ -109,32 +118,82 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   const int ip = my_row + off;
 
   u32x4 qreg[KC];
+  i32x8 q8[D / 64 > 0 ? D / 64 : 1];
+  if constexpr (FP8) {
+    // byte j of step c, half g = element 64 c + 32 g + j of the fp8 row
+    const uint8_t* qrow8 = reinterpret_cast<const uint8_t*>(p.q) + ((int64_t)q_start + my_row) * p.q_rstride + h * D;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    qreg[c] = row_ok ? gload128(qbase + (int64_t)my_row * p.q_rstride + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < D / 64; ++c) {
+      const u32x4 lo = row_ok ? gload128(qrow8 + 64 * c + 32 * g) : u32x4{0, 0, 0, 0};
+      const u32x4 hi = row_ok ? gload128(qrow8 + 64 * c + 32 * g + 16) : u32x4{0, 0, 0, 0};
+      q8[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      qreg[c] = row_ok ? gload128(qbase + (int64_t)my_row * p.q_rstride + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    }
   }
+  // FP8: the logits are scaled by the dequantisation factors of q and k
+  float dqk = 1.0f, dsv = 1.0f;
+  if constexpr (FP8) {
+    const int64_t di = (int64_t)b * (p.Hq / p.g) + hk;
+    dqk = (p.dsc_q ? p.dsc_q[di] : 1.0f) * (p.dsc_k ? p.dsc_k[di] : 1.0f);
+    dsv = p.dsc_v ? p.dsc_v[di] : 1.0f;
+  }
+  const float sl2 = p.scale_log2 * dqk, soc = p.scale_over_cap * dqk;
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
-  const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
+  const float fs = (SOFTCAP || ALIBI) ? 1.0f : sl2;
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
   const uint32_t bh = (uint32_t)(b * p.Hq + h);  // dropout counter word 2
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-    auto dma_k = [&](int t, char* dst) { dma_tile<D, BC, 4>(dst, kbase, p.k_rstride, t * BC, Sk, w, lane); };
+    auto dma_k = [&](int t, char* dst) {
+      if constexpr (FP8) {
+        // fp8 rows of D bytes copied as D / 2 16-bit elements
+        const uint16_t* kb8 = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.k) +
+                                                                (int64_t)k_start * p.k_rstride + hk * D);
+        dma_tile<(D >= 64 ? D / 2 : 32), BC, 4>(dst, kb8, p.k_rstride / 2, t * BC, Sk, w, lane);
+      } else {
+        dma_tile<D, BC, 4>(dst, kbase, p.k_rstride, t * BC, Sk, w, lane);
+      }
+    };
     auto dma_v = [&](int t, char* dst) { dma_tile<D, BC, 4>(dst, vbase, p.k_rstride, t * BC, Sk, w, lane); };
 
     // S^T = K Q^T for the 64 keys of LDS tile `kt` (raw dot products).
     auto qk = [&](const char* kt, uint32_t nbv, f32x16 (&sa)[2]) {
+      if constexpr (FP8) {
+        // A operand: key row lane % 32, bytes 64 c + 32 g .. + 31 (chunks
+        // 4c + 2g and 4c + 2g + 1 of the D-byte row, swizzled like a
+        // D/2-element 16-bit row)
+        constexpr int DH = D >= 64 ? D / 2 : 32;
+        const uint32_t nb8 = opaque(row_base<DH>(lane & 31) ^ ((uint32_t)(2 * g) << 4));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sa[kb] = f32x16{};
+        for (int kb = 0; kb < 2; ++kb) {
+          sa[kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          sa[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], sa[kb]);
+          for (int c = 0; c < D / 64; ++c) {
+            const char* t8 = kt + (kb * 32) * D;
+            const u32x4 lo = lds_read128(t8, nb8 ^ ((uint32_t)c << 6));
+            const u32x4 hi = lds_read128(t8, nb8 ^ ((uint32_t)c << 6) ^ 16u);
+            const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            sa[kb] = mfma32_fp8(ka, q8[c], sa[kb]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sa[kb] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            sa[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], sa[kb]);
+          }
         }
       }
     };
@@ -151,8 +210,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
           for (int i = 0; i < 16; ++i) {
             float x = sa[kb][i];
             const int j = j0 + 32 * kb + frag_row(i, g);
-            if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * p.scale_over_cap);
-            else x = x * p.scale_log2;
+            if constexpr (SOFTCAP) x = p.cap_log2 * tanh_exp(x * soc);
+            else x = x * sl2;
             if constexpr (ALIBI) x -= slope_log2 * (float)abs(ip - j);
             sa[kb][i] = x;
           }
@@ -309,7 +368,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     // Four distinct LDS arrays: K and V, double buffered, so reads of one are
     // never ordered behind the DMA into another.
     f32x16 sA[2], sB[2];
-    if constexpr (DROP || D >= 256) {
+    if constexpr (DROP || D >= 256 || FP8) {
       // With dropout the generator's integer work dominates the VALU, and at
       // D = 256 two S tiles next to the O accumulator exceed the register
       // file, so the tiles run one after another (S, softmax, P V) with the
@@ -359,7 +418,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
   const float l_tot = l_run + xor32(l_run);
   if (row_ok) {
-    const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) * (FP8 ? dsv : 1.0f) / l_tot : 0.0f;
     uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.o_rstride + h * D;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
@@ -392,6 +451,36 @@ static void launch_fwd_dt(const FwdParams& prm, bool softcap, bool alibi, int nw
   }
 }
 
+template <int D>
+static void launch_fwd_fp8(const FwdParams& prm, bool softcap, bool alibi, int nwg, hipStream_t st) {
+  dim3 grid(nwg), block(256);
+  if (softcap) {
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT_BF16, true, true, false, true>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT_BF16, true, false, false, true>), grid, block, 0, st, prm);
+  } else {
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT_BF16, false, true, false, true>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT_BF16, false, false, false, true>), grid, block, 0, st, prm);
+  }
+}
+
+// fp8 (OCP e4m3) -> bfloat16, 16 bytes per thread; exact, since every e4m3
+// value is a bfloat16 value.
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* src, uint16_t* dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 v = gload128(src + 16 * i);
+  uint32_t o[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);  // bytes 0, 1
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);   // bytes 2, 3
+    o[2 * e] = pack2<DT_BF16>(a[0], a[1]);
+    o[2 * e + 1] = pack2<DT_BF16>(b[0], b[1]);
+  }
+  gstore128(dst + 16 * i, u32x4{o[0], o[1], o[2], o[3]});
+  gstore128(dst + 16 * i + 8, u32x4{o[4], o[5], o[6], o[7]});
+}
+
 template <int D, int DT>
 static void launch_fwd_d(const FwdParams& prm, bool softcap, bool alibi, bool drop, int nwg, hipStream_t st) {
   if (drop) launch_fwd_dt<D, DT, true>(prm, softcap, alibi, nwg, st);
@@ -399,7 +488,7 @@ static void launch_fwd_d(const FwdParams& prm, bool softcap, bool alibi, bool dr
 }
 
 static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap, int causal,
-                   int max_sq, int nbatch, hipStream_t st) {
+                   int max_sq, int nbatch, hipStream_t st, bool fp8 = false) {
   prm.scale_log2 = scale * kLog2e;
   prm.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
   prm.cap_log2 = softcap * kLog2e;
@@ -414,6 +503,12 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
   const bool sc = softcap > 0.0f, al = prm.alibi != nullptr, dr = prm.drop.t > 0;
   prof_before(FA_KERNEL_FWD, st);
   const bool bf = dtype == FA_DTYPE_BF16;
+  if (fp8) {
+    if (D == 128) launch_fwd_fp8<128>(prm, sc, al, (int)nwg, st);
+    else launch_fwd_fp8<64>(prm, sc, al, (int)nwg, st);
+    prof_after(FA_KERNEL_FWD, st);
+    return launch_status();
+  }
   switch (D) {
     case 32:
       if (bf) launch_fwd_d<32, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
@@ -551,6 +646,55 @@ extern "C" int fa_fwd_kvpacked(const void* q, const void* kv, void* out, float* 
   return fwd_dense(q, base, base + Hkv * D, out, lse, B, Sq, Sk, Hq, Hkv, D, dtype, scale, causal,
                    window_left, window_right, softcap, alibi_slopes, DropSpec{}, stream,
                    RowStrides{0, 2 * Hkv * D, 0});
+}
+
+extern "C" size_t fa_fwd_fp8_workspace_size(int B, int Sk, int Hkv, int D) {
+  if (B < 1 || Sk < 1 || Hkv < 1 || D < 1) return 0;
+  return align_up((size_t)B * Sk * Hkv * D * 2, 256);
+}
+
+extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                          float scale, int causal, int window_left, int window_right, float softcap,
+                          const float* alibi_slopes, const float* descale_q, const float* descale_k,
+                          const float* descale_v, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(Hq, Hkv, D, FA_DTYPE_BF16, scale, window_left, window_right, softcap);
+  if (st) return st;
+  if (B < 1 || Sq < 1 || Sk < 1) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
+  if ((descale_q && !aligned4(descale_q)) || (descale_k && !aligned4(descale_k)) ||
+      (descale_v && !aligned4(descale_v)))
+    return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_fwd_fp8_workspace_size(B, Sk, Hkv, D);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  // V: fp8 -> bfloat16 copy in the workspace (exact)
+  const int64_t n16 = (int64_t)B * Sk * Hkv * D / 16;
+  hipLaunchKernelGGL(fp8_to_bf16_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     (const uint8_t*)v, (uint16_t*)workspace, n16);
+  FwdParams prm{};
+  prm.q = (const uint16_t*)q;  // fp8 bytes, read as such by the FP8 kernel
+  prm.k = (const uint16_t*)k;
+  prm.v = (const uint16_t*)workspace;
+  prm.o = (uint16_t*)out;
+  prm.lse = lse;
+  prm.Sq = Sq;
+  prm.Sk = Sk;
+  prm.Hq = Hq;
+  prm.g = Hq / Hkv;
+  prm.q_rstride = Hq * D;
+  prm.k_rstride = Hkv * D;
+  prm.o_rstride = Hq * D;
+  prm.alibi = alibi_slopes;
+  prm.wl = window_left;
+  prm.wr = window_right;
+  prm.dsc_q = descale_q;
+  prm.dsc_k = descale_k;
+  prm.dsc_v = descale_v;
+  return run_fwd(prm, D, FA_DTYPE_BF16, scale, softcap, causal, Sq, B, s, true);
 }
 
 extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
