@@ -164,8 +164,8 @@ def run_fwdbwd(args, torch, fa):
                          "tflops": round(fl / ms / 1e9, 1)})
     # other head dims at hidden 2048 (H = 2048 / D), S = 4K, B = 4
     by_d = []
-    for Dh in (32, 64, 256):
-        Hh = 2048 // Dh
+    for Dh in (32, 64, 96, 256):
+        Hh = 2048 // Dh if 2048 % Dh == 0 else 24  # D = 96: 24 heads (hidden 2304)
         g = torch.Generator().manual_seed(2)
         mk = lambda: torch.randn(4, 4096, Hh, Dh, generator=g).to(torch.bfloat16).to(dev)
         q_, k_, v_, do_ = mk(), mk(), mk(), mk()

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* a size, pointer, option or alignment is invalid */
-  FA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (e.g. D = 96) */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (e.g. D = 80) */
   FA_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than the size query */
   FA_ERR_LAUNCH = 4       /* hipGetLastError reported an error after a launch */
 } fa_status;
@@ -69,7 +69,8 @@ const char* fa_status_string(int status);
  *   q (B,Sq,Hq,D), k/v (B,Sk,Hkv,D) in: 16-bit, read only.
  *   out (B,Sq,Hq,D) out: 16-bit, rounded once from float32.
  *   lse (B,Hq,Sq) out: float32; may be NULL when the caller does not need it.
- *   D in {64, 128}; scale > 0 finite; softcap >= 0 (0 = off);
+ *   D in {32, 64, 96, 128, 256} (96 runs on the 128-wide kernels with the
+ *   head padded on chip); scale > 0 finite; softcap >= 0 (0 = off);
  *   alibi_slopes: NULL or float32 (Hq,) device array, one slope per query head.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,

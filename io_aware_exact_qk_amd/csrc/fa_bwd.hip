@@ -92,15 +92,19 @@ __device__ __forceinline__ int64_t row_index(const BwdParams& p, int b, int h, i
 // One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).  Writes
 // delta = sum_d dO O and the forward's LSE in log2 units, the two per-row
 // values the recompute kernels need.
+// A head's D / 8 chunks go to NCH lanes, rounded up to a power of two for the
+// shuffle reduction (D = 96: 16 lanes, 12 of them loading).
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+
 template <int D, int DT>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int NCH = D / 8;
+  constexpr int NCH = pow2_at_least(D / 8);
   const int gid = (blockIdx.x * 256 + threadIdx.x) / NCH;
   const int ch = threadIdx.x % NCH;
   const int token = gid / p.Hq, h = gid % p.Hq;
   const bool ok = token < p.n_tokens;
   float acc = 0.0f;
-  if (ok) {
+  if (ok && ch < D / 8) {
     const int64_t base = (int64_t)token * p.o_rstride + h * D + ch * 8;
     const u32x4 a = gload128(p.o + base);
     const u32x4 c = gload128(p.dout + base);
@@ -153,7 +157,8 @@ __device__ __forceinline__ float softcap_grad(float ds, float pv, float x, int i
 // the VGPRs two waves per SIMD need).  Query tiles of 64 rows (Q, dO, LSE,
 // delta) are copied into LDS by DMA, double buffered; the copy of tile n+1
 // runs under the matrix work of tile n.
-template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
+// DG < D: head dim DG in memory, padded to D on chip (see fwd_kernel).
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP, int DG = D>
 __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = DkdvShape<D>::NW, BC = 32 * NW, BR = DkdvShape<D>::BR;
   constexpr int KC = D / 16, DB = D / 32;
@@ -184,13 +189,19 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   const int kw0 = k0 + 32 * w;
   const int my_key = kw0 + r;
   const bool key_ok = my_key < Sk;
-  const int64_t krow = (int64_t)(sb.k_start + my_key) * p.k_rstride + hk * D;
+  const int64_t krow = (int64_t)(sb.k_start + my_key) * p.k_rstride + hk * DG;
 
   u32x4 kreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    kreg[c] = key_ok ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    const bool in = DG == D || (2 * c + g) * 8 < DG;
+    kreg[c] = (key_ok && in) ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
+  zero_pad<D, BC, DG>(vsm, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm0, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm0 + TILE, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm1, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm1 + TILE, tid, 64 * NW);
   const char* vw = vsm + (32 * w) * (D * 2);  // this wave's 32 V rows
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -210,10 +221,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
     auto issue = [&](int n, char* st) {
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
-      const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * D;
-      const int64_t ooff = (int64_t)sb.q_start * p.o_rstride + (int64_t)hq * D;
-      dma_tile<D, BR, NW>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
-      dma_tile<D, BR, NW>(st + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
+      const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * DG;
+      const int64_t ooff = (int64_t)sb.q_start * p.o_rstride + (int64_t)hq * DG;
+      dma_tile<D, BR, NW, true, DG>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW, true, DG>(st + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
         const int i = min(i0 + lane, Sq - 1);
@@ -305,7 +316,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
     };
 
     // V rows past Sk hold a copy of the last row; their keys are masked
-    dma_tile<D, BC, NW>(vsm, p.v + (int64_t)sb.k_start * p.k_rstride + hk * D, p.k_rstride, k0, Sk, w, lane);
+    dma_tile<D, BC, NW, true, DG>(vsm, p.v + (int64_t)sb.k_start * p.k_rstride + hk * DG, p.k_rstride, k0, Sk,
+                                  w, lane);
     issue(0, sm0);
     dma_wait();
     __syncthreads();
@@ -318,11 +330,12 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   }
 
   if (key_ok) {
-    const int64_t drow_off = (int64_t)(sb.k_start + my_key) * p.dkv_rstride + hk * D;
+    const int64_t drow_off = (int64_t)(sb.k_start + my_key) * p.dkv_rstride + hk * DG;
     uint16_t* dkrow = p.dk + drow_off;
     uint16_t* dvrow = p.dv + drow_off;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
+      if (32 * d >= DG) continue;  // padded columns
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 a, c;
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
 // Work-group = 128 query rows of one query head (4 waves of 32 rows), two
 // work-groups per CU; K/V tiles of 64 keys are copied into LDS by DMA,
 // double buffered.
-template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP>
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP, int DG = D>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16, DB = D / 32;
@@ -371,15 +384,20 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   const int my_row = wrow0 + r;
   const bool row_ok = my_row < Sq;
   const int ip = my_row + off;
-  const int64_t qrow = (int64_t)(sb.q_start + my_row) * p.q_rstride + h * D;
-  const int64_t orow = (int64_t)(sb.q_start + my_row) * p.o_rstride + h * D;
+  const int64_t qrow = (int64_t)(sb.q_start + my_row) * p.q_rstride + h * DG;
+  const int64_t orow = (int64_t)(sb.q_start + my_row) * p.o_rstride + h * DG;
 
   u32x4 qreg[KC], doreg[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    qreg[c] = row_ok ? gload128(p.q + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
-    doreg[c] = row_ok ? gload128(p.dout + orow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    const bool in = row_ok && (DG == D || (2 * c + g) * 8 < DG);
+    qreg[c] = in ? gload128(p.q + qrow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+    doreg[c] = in ? gload128(p.dout + orow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
+  zero_pad<D, BC, DG>(sm0, tid, 256);
+  zero_pad<D, BC, DG>(sm0 + TILE, tid, 256);
+  zero_pad<D, BC, DG>(sm1, tid, 256);
+  zero_pad<D, BC, DG>(sm1 + TILE, tid, 256);
   float lse2 = INFINITY, dv_row = 0.0f;  // rows past the end: P = 0
   if (row_ok) {
     const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
@@ -397,14 +415,14 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   int kv_lo = 0, kv_hi = Sk;
   if (p.wl >= 0) kv_lo = max(0, q0 + off - p.wl);
   if (p.wr >= 0) kv_hi = min(Sk, qend - 1 + off + p.wr + 1);
-  const uint16_t* kbase = p.k + (int64_t)sb.k_start * p.k_rstride + hk * D;
-  const uint16_t* vbase = p.v + (int64_t)sb.k_start * p.k_rstride + hk * D;
+  const uint16_t* kbase = p.k + (int64_t)sb.k_start * p.k_rstride + hk * DG;
+  const uint16_t* vbase = p.v + (int64_t)sb.k_start * p.k_rstride + hk * DG;
 
   if (kv_lo < kv_hi) {
     const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
     auto issue = [&](int t, char* kt) {
-      dma_tile<D, BC, 4, false>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
-      dma_tile<D, BC, 4, false>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4, false, DG>(kt, kbase, p.k_rstride, t * BC, Sk, w, lane);
+      dma_tile<D, BC, 4, false, DG>(kt + TILE, vbase, p.k_rstride, t * BC, Sk, w, lane);
     };
     // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
     auto step = [&](const char* kt, char* nxt, int t) {
@@ -482,9 +500,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   }
 
   if (row_ok) {
-    uint16_t* drow = p.dq + (int64_t)(sb.q_start + my_row) * p.dq_rstride + h * D;
+    uint16_t* drow = p.dq + (int64_t)(sb.q_start + my_row) * p.dq_rstride + h * DG;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
+      if (32 * d >= DG) continue;  // padded columns
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 v2;
@@ -497,43 +516,44 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
 }
 
 // ------------------------------------------------------------- dispatch ---
-template <int D, int DT, bool SC, bool AL, bool DR>
+template <int D, int DT, bool SC, bool AL, bool DR, int DG>
 static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
   if (nwg_kv > 0) {
     prof_before(FA_KERNEL_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR>), dim3(nwg_kv), dim3(64 * DkdvShape<D>::NW), 0, st,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR, DG>), dim3(nwg_kv), dim3(64 * DkdvShape<D>::NW), 0, st,
                        dkdv);
     prof_after(FA_KERNEL_BWD_DKDV, st);
   }
   if (nwg_q > 0) {
     prof_before(FA_KERNEL_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL, DR>), dim3(nwg_q), dim3(256), 0, st, dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL, DR, DG>), dim3(nwg_q), dim3(256), 0, st, dq);
     prof_after(FA_KERNEL_BWD_DQ, st);
   }
 }
 
-template <int D, int DT, bool SC, bool AL>
+template <int D, int DT, bool SC, bool AL, int DG>
 static void launch_main_d(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, bool dr,
                           hipStream_t st) {
-  if (dr) launch_main<D, DT, SC, AL, true>(dkdv, dq, nwg_kv, nwg_q, st);
-  else launch_main<D, DT, SC, AL, false>(dkdv, dq, nwg_kv, nwg_q, st);
+  if (dr) launch_main<D, DT, SC, AL, true, DG>(dkdv, dq, nwg_kv, nwg_q, st);
+  else launch_main<D, DT, SC, AL, false, DG>(dkdv, dq, nwg_kv, nwg_q, st);
 }
 
-template <int D, int DT>
+// D: the head dim on chip; DG: in memory (DG < D only for D = 96 on 128)
+template <int D, int DT, int DG = D>
 static void launch_all(const BwdParams& pre, int nwg_pre, const BwdParams& dkdv, const BwdParams& dq,
                        int nwg_kv, int nwg_q, bool sc, bool al, hipStream_t st) {
   if (nwg_pre > 0) {
     prof_before(FA_KERNEL_BWD_PREPROCESS, st);
-    hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3(nwg_pre), dim3(256), 0, st, pre);
+    hipLaunchKernelGGL((bwd_pre_kernel<DG, DT>), dim3(nwg_pre), dim3(256), 0, st, pre);
     prof_after(FA_KERNEL_BWD_PREPROCESS, st);
   }
   const bool dr = dkdv.drop.t > 0;
   if (sc) {
-    if (al) launch_main_d<D, DT, true, true>(dkdv, dq, nwg_kv, nwg_q, dr, st);
-    else launch_main_d<D, DT, true, false>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    if (al) launch_main_d<D, DT, true, true, DG>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    else launch_main_d<D, DT, true, false, DG>(dkdv, dq, nwg_kv, nwg_q, dr, st);
   } else {
-    if (al) launch_main_d<D, DT, false, true>(dkdv, dq, nwg_kv, nwg_q, dr, st);
-    else launch_main_d<D, DT, false, false>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    if (al) launch_main_d<D, DT, false, true, DG>(dkdv, dq, nwg_kv, nwg_q, dr, st);
+    else launch_main_d<D, DT, false, false, DG>(dkdv, dq, nwg_kv, nwg_q, dr, st);
   }
 }
 
@@ -542,7 +562,7 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   if (causal) base.wr = 0;
   BwdParams pre = base;
   pre.n_tokens = n_tokens;
-  const long long pre_threads = (long long)n_tokens * base.Hq * (D / 8);
+  const long long pre_threads = (long long)n_tokens * base.Hq * pow2_at_least(D / 8);
   const long long nwg_pre = (pre_threads + 255) / 256;
   BwdParams kv = base;
   const int kv_keys = 32 * (D >= 256 ? DkdvShape<256>::NW : DkdvShape<128>::NW);
@@ -571,6 +591,10 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
     case 64:
       if (bf) launch_all<64, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
       else launch_all<64, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      break;
+    case 96:  // padded to 128 on chip
+      if (bf) launch_all<128, DT_BF16, 96>(pre, np, kv, dq, nk, nq, sc, al, st);
+      else launch_all<128, DT_F16, 96>(pre, np, kv, dq, nk, nq, sc, al, st);
       break;
     case 128:
       if (bf) launch_all<128, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);

@@ -277,7 +277,10 @@ constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 // between tiles; otherwise rows at or past `nrows` (>= 1) re-read row
 // nrows - 1 (valid memory) and callers mask those rows.  FAST = false always
 // takes the clamped form (fewer live values, for kernels at the VGPR limit).
-template <int D, int ROWS, int NWAVES, bool FAST = true>
+// DG < D: rows hold DG elements in memory and are padded to D on chip; the
+// lanes of logical chunks >= DG / 8 copy nothing (those slots are zeroed
+// once by zero_pad and never written again).
+template <int D, int ROWS, int NWAVES, bool FAST = true, int DG = D>
 __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64_t rstride, int row0,
                                          int nrows, int w, int lane) {
   constexpr int NCH = D / 8, RPB = 64 / NCH, NBLK = ROWS / RPB;
@@ -295,7 +298,7 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64
       // re-derived per call: hoisting whole 64-bit addresses out of the tile
       // loop would cost two VGPRs per block
       const uint32_t loff = opaque((uint32_t)(rin * rstride + ((pch ^ (int)swz<D>(row)) << 3)) * 2u);
-      dma16(b0 + (int64_t)blk * RPB * rstride * 2 + loff, tile + blk * 1024);
+      if (DG == D || (pch ^ (int)swz<D>(row)) < DG / 8) dma16(b0 + (int64_t)blk * RPB * rstride * 2 + loff, tile + blk * 1024);
     }
   } else {
 #pragma unroll
@@ -304,7 +307,21 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64
       const int row = blk * RPB + rin;
       const int lch = pch ^ (int)swz<D>(row);
       const int grow = min(row0 + row, nrows - 1);
-      dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+      if (DG == D || lch < DG / 8) dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+    }
+  }
+}
+
+// Zero the 16-byte slots of a ROWS x D tile that hold logical chunks
+// >= DG / 8 (a head dim DG < D padded to D on chip).  The DMA never writes
+// them, so one pass before the first barrier keeps them zero for good.
+template <int D, int ROWS, int DG>
+__device__ __forceinline__ void zero_pad(char* tile, int tid, int nthreads) {
+  if constexpr (DG < D) {
+    constexpr int PAD = D / 8 - DG / 8;
+    for (int i = tid; i < ROWS * PAD; i += nthreads) {
+      const int row = i / PAD, lch = DG / 8 + i % PAD;
+      lds_write128(tile, tile_off<D>(row, lch), u32x4{0, 0, 0, 0});
     }
   }
 }

@@ -62,7 +62,10 @@ struct FwdParams {
 // fp8 Q fragments and fp8 K tiles; P V stays in bfloat16 (V converted
 // exactly beforehand), so only the logits change precision and they are
 // exact products of the fp8 inputs.
-template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP, bool FP8 = false>
+// DG < D: the head dim in memory is DG and is padded to D on chip (zero Q
+// columns and zero K/V tile columns, so S and the first DG columns of O are
+// exact; the rest is never stored).
+template <int D, int DT, bool SOFTCAP, bool ALIBI, bool DROP, bool FP8 = false, int DG = D>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p) {
   constexpr int BR = 128, BC = 64;
   constexpr int KC = D / 16;               // MFMA steps along D
@@ -102,9 +105,9 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   const int off = Sk - Sq;
   const MaskSpec mask{p.wl, p.wr};
 
-  const uint16_t* qbase = p.q + (int64_t)q_start * p.q_rstride + h * D;
-  const uint16_t* kbase = p.k + (int64_t)k_start * p.k_rstride + hk * D;
-  const uint16_t* vbase = p.v + (int64_t)k_start * p.k_rstride + hk * D;
+  const uint16_t* qbase = p.q + (int64_t)q_start * p.q_rstride + h * DG;
+  const uint16_t* kbase = p.k + (int64_t)k_start * p.k_rstride + hk * DG;
+  const uint16_t* vbase = p.v + (int64_t)k_start * p.k_rstride + hk * DG;
 
   const int qend = min(q0 + BR, Sq);
   int kv_lo = 0, kv_hi = Sk;
@@ -131,7 +134,9 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   } else {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      qreg[c] = row_ok ? gload128(qbase + (int64_t)my_row * p.q_rstride + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+      const bool in = DG == D || (2 * c + g) * 8 < DG;
+      qreg[c] = (row_ok && in) ? gload128(qbase + (int64_t)my_row * p.q_rstride + (2 * c + g) * 8)
+                               : u32x4{0, 0, 0, 0};
     }
   }
   // FP8: the logits are scaled by the dequantisation factors of q and k
@@ -160,10 +165,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
                                                                 (int64_t)k_start * p.k_rstride + hk * D);
         dma_tile<(D >= 64 ? D / 2 : 32), BC, 4>(dst, kb8, p.k_rstride / 2, t * BC, Sk, w, lane);
       } else {
-        dma_tile<D, BC, 4>(dst, kbase, p.k_rstride, t * BC, Sk, w, lane);
+        dma_tile<D, BC, 4, true, DG>(dst, kbase, p.k_rstride, t * BC, Sk, w, lane);
       }
     };
-    auto dma_v = [&](int t, char* dst) { dma_tile<D, BC, 4>(dst, vbase, p.k_rstride, t * BC, Sk, w, lane); };
+    auto dma_v = [&](int t, char* dst) {
+      dma_tile<D, BC, 4, true, DG>(dst, vbase, p.k_rstride, t * BC, Sk, w, lane);
+    };
 
     // S^T = K Q^T for the 64 keys of LDS tile `kt` (raw dot products).
     auto qk = [&](const char* kt, uint32_t nbv, f32x16 (&sa)[2]) {
@@ -368,6 +375,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     // Four distinct LDS arrays: K and V, double buffered, so reads of one are
     // never ordered behind the DMA into another.
     f32x16 sA[2], sB[2];
+    zero_pad<D, BC, DG>(kb0, tid, 256);
+    zero_pad<D, BC, DG>(kb1, tid, 256);
+    zero_pad<D, BC, DG>(vb0, tid, 256);
+    zero_pad<D, BC, DG>(vb1, tid, 256);
     if constexpr (DROP || D >= 256 || FP8) {
       // With dropout the generator's integer work dominates the VALU, and at
       // D = 256 two S tiles next to the O accumulator exceed the register
@@ -419,9 +430,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   const float l_tot = l_run + xor32(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) * (FP8 ? dsv : 1.0f) / l_tot : 0.0f;
-    uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.o_rstride + h * D;
+    uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.o_rstride + h * DG;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
+      if (32 * d >= DG) continue;  // padded columns
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 v2;
@@ -439,15 +451,15 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   }
 }
 
-template <int D, int DT, bool DROP>
+template <int D, int DT, bool DROP, int DG = D>
 static void launch_fwd_dt(const FwdParams& prm, bool softcap, bool alibi, int nwg, hipStream_t st) {
   dim3 grid(nwg), block(256);
   if (softcap) {
-    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, true, true, DROP>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((fwd_kernel<D, DT, true, false, DROP>), grid, block, 0, st, prm);
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, true, true, DROP, false, DG>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, true, false, DROP, false, DG>), grid, block, 0, st, prm);
   } else {
-    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, false, true, DROP>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((fwd_kernel<D, DT, false, false, DROP>), grid, block, 0, st, prm);
+    if (alibi) hipLaunchKernelGGL((fwd_kernel<D, DT, false, true, DROP, false, DG>), grid, block, 0, st, prm);
+    else hipLaunchKernelGGL((fwd_kernel<D, DT, false, false, DROP, false, DG>), grid, block, 0, st, prm);
   }
 }
 
@@ -481,10 +493,10 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* src, ui
   gstore128(dst + 16 * i + 8, u32x4{o[4], o[5], o[6], o[7]});
 }
 
-template <int D, int DT>
+template <int D, int DT, int DG = D>
 static void launch_fwd_d(const FwdParams& prm, bool softcap, bool alibi, bool drop, int nwg, hipStream_t st) {
-  if (drop) launch_fwd_dt<D, DT, true>(prm, softcap, alibi, nwg, st);
-  else launch_fwd_dt<D, DT, false>(prm, softcap, alibi, nwg, st);
+  if (drop) launch_fwd_dt<D, DT, true, DG>(prm, softcap, alibi, nwg, st);
+  else launch_fwd_dt<D, DT, false, DG>(prm, softcap, alibi, nwg, st);
 }
 
 static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap, int causal,
@@ -517,6 +529,10 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
     case 64:
       if (bf) launch_fwd_d<64, DT_BF16>(prm, sc, al, dr, (int)nwg, st);
       else launch_fwd_d<64, DT_F16>(prm, sc, al, dr, (int)nwg, st);
+      break;
+    case 96:  // padded to 128 on chip
+      if (bf) launch_fwd_d<128, DT_BF16, 96>(prm, sc, al, dr, (int)nwg, st);
+      else launch_fwd_d<128, DT_F16, 96>(prm, sc, al, dr, (int)nwg, st);
       break;
     case 128:
       if (bf) launch_fwd_d<128, DT_BF16>(prm, sc, al, dr, (int)nwg, st);

@@ -23,7 +23,7 @@ inline int check_common(int Hq, int Hkv, int D, int dtype, float scale, int wl, 
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (wl < -1 || wr < -1) return FA_ERR_INVALID_ARG;
   if (!(softcap >= 0.0f) || !isfinite(softcap)) return FA_ERR_INVALID_ARG;
-  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 96 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -1,4 +1,4 @@
-"""Head dims 32 and 256 (besides 64 and 128): forward and backward parity
+"""Head dims 32, 96 and 256 (besides 64 and 128): forward and backward parity
 with the oracle over the option mixes, varlen, dropout and the packed entry
 points, at sizes that span several tiles with ragged tails.  Outputs use the
 rounding-aware bound of _helpers.assert_out_rounded (short causal rows)."""
@@ -21,6 +21,8 @@ CASES = [
     (2, 130, 257, 8, 2, 32, "bf16", True, (-1, -1), 0.0, False),
     (1, 300, 300, 2, 2, 32, "fp16", False, (17, 33), 5.0, True),
     (1, 1, 1, 1, 1, 256, "bf16", False, (-1, -1), 0.0, False),
+    (2, 200, 200, 4, 2, 96, "bf16", True, (-1, -1), 0.0, False),
+    (1, 257, 190, 4, 4, 96, "fp16", False, (64, 7), 20.0, True),
 ]
 
 
@@ -55,7 +57,7 @@ def test_fwd_bwd(case):
     assert_grad(dv, gv, "dv")
 
 
-@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("D", [32, 96, 256])
 def test_varlen(D):
     c = varlen_case([300, 77, 1, 190], Hq=4, Hkv=2, D=D, seed=1100 + D, causal=True)
     q, k, v, do = (t.to(DEV) for t in (c.q, c.k, c.v, c.dout))
@@ -74,7 +76,7 @@ def test_varlen(D):
     assert_grad(dv, gv, "dv")
 
 
-@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("D", [32, 96, 256])
 def test_dropout_and_packed(D):
     c = dense_case(1, 160, 160, 2, 2, D, "bf16", seed=1200 + D, causal=True)
     q, k, v, do = (t.to(DEV) for t in (c.q, c.k, c.v, c.dout))
@@ -97,7 +99,7 @@ def test_dropout_and_packed(D):
 
 
 def test_decode_rejects_unbuilt_head_dims():
-    for D in (32, 256):
+    for D in (32, 96, 256):
         q = torch.zeros(1, 1, 4, D, dtype=torch.bfloat16, device=DEV)
         kc = torch.zeros(1, 64, 4, D, dtype=torch.bfloat16, device=DEV)
         sl = torch.ones(1, dtype=torch.int32, device=DEV)

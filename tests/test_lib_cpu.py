@@ -70,7 +70,7 @@ def _fwd(lib, **kw):
     (dict(Hq=3, Hkv=2), 1), (dict(Hkv=0), 1), (dict(dtype=2), 1), (dict(scale=0.0), 1),
     (dict(scale=float("inf")), 1), (dict(wl=-2), 1), (dict(softcap=-1.0), 1),
     (dict(softcap=float("nan")), 1), (dict(B=0), 1), (dict(Sq=0), 1),
-    (dict(q=ctypes.c_void_p(A + 8)), 1), (dict(out=None), 1), (dict(D=96), 2), (dict(D=48), 2),
+    (dict(q=ctypes.c_void_p(A + 8)), 1), (dict(out=None), 1), (dict(D=80), 2), (dict(D=48), 2),
 ])
 def test_fwd_rejects_invalid(lib, kw, status):
     assert _fwd(lib, **kw) == status
