@@ -245,7 +245,8 @@ int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const voi
  * flash_attn_with_kvcache"): the new k/v are appended to the cache in place
  * and the new queries attend over the cache plus the appended tokens.
  *   q (B, Sq_new, Hq, D) in; (Hq / Hkv) * Sq_new <= 32 (the new queries of
- *     one K/V head are the 32 columns of one matrix tile), D in {64, 128}.
+ *     one K/V head are the 32 columns of one matrix tile), D in
+ *     {32, 64, 96, 128} (96 padded to 128 on chip).
  *   k_new/v_new (B, Sq_new, Hkv, D) in, or both NULL (attend without append).
  *   k_cache/v_cache in/out: paged (n_pages, page_size, Hkv, D) when
  *     block_table != NULL, else contiguous (B, max_blocks_per_seq*page_size, Hkv, D).

@@ -93,12 +93,16 @@ constexpr int kDecodeSortMax = 64;
 // window w to keys >= position - w.  OPTS: softcap, ALiBi or a window is on.
 // With T > 1 the appended rows were written by decode_append_kernel before
 // this kernel starts; with T = 1 the kernel appends in its own prologue.
-template <int D, int DT, bool OPTS>
+// DG < D: head dim DG in memory padded to D on chip (zero fragments and tile
+// columns past DG).
+template <int D, int DT, bool OPTS, int DG = D>
 __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int BK = 32;  // keys per wave tile
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int VT = BK * D * 2;  // bytes of one wave's V tile
-  constexpr int NVM = KC + VT / 1024;  // vector-memory instructions per tile load
+  // vector-memory instructions per tile load (K fragments past DG are not loaded)
+  constexpr int NKL = DG == D ? KC : (DG + 15) / 16;
+  constexpr int NVM = NKL + VT / 1024;
   // V tiles, one per wave and stage; four distinct arrays (one per stage) so
   // a read of one stage is never ordered behind the DMA into another.
   __shared__ __attribute__((aligned(1024))) char vs0[4 * VT];
@@ -163,19 +167,27 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int NCH = D / 8;
   const int hr = p.cos ? p.rotary_dim / 2 : 0;  // rotary half width (0 = off)
   {
+    // chunks past DG / 8 are written as zeros (padded head dim)
     const int nq = G * T * NCH, nk = fused ? NCH : 0;
     for (int i = tid; i < nq + nk; i += 256) {
       if (i < nq) {
         const int row = i / NCH, ch = i % NCH;  // row = column t * G + g
         const int t = row / G, gq = row % G;
-        const u32x4 v = gload128(p.q + (((int64_t)b * T + t) * p.Hq + hkv * G + gq) * D + ch * 8);
+        const u32x4 v = (DG == D || ch < DG / 8)
+                            ? gload128(p.q + (((int64_t)b * T + t) * p.Hq + hkv * G + gq) * DG + ch * 8)
+                            : u32x4{0, 0, 0, 0};
         lds_write128(qst, (row * D + ch * 8) * 2, v);
       } else {
         const int ch = i - nq;
-        const u32x4 v = gload128(p.k_new + ((int64_t)b * p.Hkv + hkv) * D + ch * 8);
+        const u32x4 v = (DG == D || ch < DG / 8) ? gload128(p.k_new + ((int64_t)b * p.Hkv + hkv) * DG + ch * 8)
+                                                 : u32x4{0, 0, 0, 0};
         lds_write128(qst, (32 * D + ch * 8) * 2, v);
       }
     }
+    zero_pad<D, 4 * BK, DG>(vs0, tid, 256);
+    zero_pad<D, 4 * BK, DG>(vs1, tid, 256);
+    zero_pad<D, 4 * BK, DG>(vs2, tid, 256);
+    zero_pad<D, 4 * BK, DG>(vs3, tid, 256);
     __syncthreads();
   }
   // Chunk ch (8 elements) of a staged row, rotated at position pos: the
@@ -244,11 +256,11 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   auto tile_base = [&](int j0) -> int64_t {
     if (p.block_table) {
       const int phys = ((const cint*)p.block_table)[(int64_t)b * p.max_blocks + j0 / page];
-      return (((int64_t)phys * page + (j0 % page)) * p.Hkv + hkv) * D;
+      return (((int64_t)phys * page + (j0 % page)) * p.Hkv + hkv) * DG;
     }
-    return (((int64_t)b * cap + j0) * p.Hkv + hkv) * D;
+    return (((int64_t)b * cap + j0) * p.Hkv + hkv) * DG;
   };
-  const int64_t kvstride = (int64_t)p.Hkv * D;
+  const int64_t kvstride = (int64_t)p.Hkv * DG;
 
   // Tiles of this split, dealt round robin to the 4 waves.
   const int t_lo = k_lo / BK, t_hi = (k_hi + BK - 1) / BK;
@@ -261,8 +273,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     const int64_t base = tile_base(t * BK);
     const uint16_t* krow = p.k_cache + base + (int64_t)r * kvstride;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) ka[c] = gload128(krow + (2 * c + hf) * 8);
-    dma_tile<D, BK, 1>(vdst, p.v_cache + base, kvstride, 0, BK, 0, lane);
+    for (int c = 0; c < KC; ++c) {
+      // padded head dim: the fragments past DG are zero (and not loaded, so
+      // the vector-memory count per tile is NKL + V blocks)
+      if (DG == D || c < NKL) ka[c] = (DG == D || (2 * c + hf) * 8 < DG) ? gload128(krow + (2 * c + hf) * 8)
+                                                                          : u32x4{0, 0, 0, 0};
+      else ka[c] = u32x4{0, 0, 0, 0};
+    }
+    dma_tile<D, BK, 1, true, DG>(vdst, p.v_cache + base, kvstride, 0, BK, 0, lane);
   };
 
   // One tile: `ka` / `vt` hold K and V of tile t.
@@ -344,18 +362,23 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   // wave or work-group reads that slot) and parks both rows in LDS for the
   // tile that uses them.
   if (fused && L >= k_lo && L < k_hi && ((L / BK - t_lo) & 3) == w && r == L % BK) {
-    const uint16_t* vnr = p.v_new + ((int64_t)b * p.Hkv + hkv) * D;
+    const uint16_t* vnr = p.v_new + ((int64_t)b * p.Hkv + hkv) * DG;
     const int64_t slot = tile_base(L - L % BK) + (int64_t)r * kvstride;
     u32x4 vv[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) vv[c] = gload128(vnr + (2 * c + hf) * 8);
+    for (int c = 0; c < KC; ++c) {
+      const bool in = DG == D || (2 * c + hf) * 8 < DG;
+      vv[c] = in ? gload128(vnr + (2 * c + hf) * 8) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       float x[8];
       rot8(qst + 32 * (D * 2), 2 * c + hf, L, x);
       const u32x4 kk = pack8<DT>(x);
-      gstore128(p.k_cache + slot + (2 * c + hf) * 8, kk);
-      gstore128(p.v_cache + slot + (2 * c + hf) * 8, vv[c]);
+      if (DG == D || (2 * c + hf) * 8 < DG) {
+        gstore128(p.k_cache + slot + (2 * c + hf) * 8, kk);
+        gstore128(p.v_cache + slot + (2 * c + hf) * 8, vv[c]);
+      }
       lds_write128(apbuf, (2 * c + hf) * 16, kk);
       lds_write128(apbuf + 2 * D, (2 * c + hf) * 16, vv[c]);
     }
@@ -420,8 +443,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     __syncthreads();
   }
   // ---- write: each thread handles (column, d) pairs ----
-  for (int idx = tid; idx < G * T * D; idx += 256) {
-    const int col = idx / D, d = idx % D;
+  for (int idx = tid; idx < G * T * DG; idx += 256) {
+    const int col = idx / DG, d = idx % DG;
     const int h = hkv * G + col % G, tt = col / G;
     const int64_t bht = ((int64_t)b * p.Hq + h) * T + tt;  // (b, h, t) of lse and partials
     float Mc = -INFINITY;
@@ -436,13 +459,13 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     }
     const float o = lc > 0.0f ? obuf[d * 32 + col] / lc : 0.0f;
     if (p.num_splits == 1) {
-      uint16_t* orow = p.out + (((int64_t)b * T + tt) * p.Hq + h) * D;
+      uint16_t* orow = p.out + (((int64_t)b * T + tt) * p.Hq + h) * DG;
       const uint32_t pk = pack2<DT>(o, 0.0f);
       orow[d] = (uint16_t)(pk & 0xffff);
       if (d == 0 && p.lse) p.lse[bht] = lc > 0.0f ? (Mc + fast_log2(lc)) * kLn2 : INFINITY;
     } else {
       const int64_t pi = bht * p.num_splits + s_id;
-      p.ws_o[pi * D + d] = o;
+      p.ws_o[pi * DG + d] = o;
       if (d == 0) p.ws_lse[pi] = lc > 0.0f ? (Mc + fast_log2(lc)) * kLn2 : -INFINITY;
     }
   }
@@ -567,21 +590,22 @@ __global__ __launch_bounds__(256) void decode_append_kernel(DecParams p) {
   gstore128(p.v_cache + slot + d0, gload128(p.v_new + src + d0));
 }
 
-template <int D, int DT>
+// D: head dim on chip; DG: in memory (96 runs padded on the 128 kernel)
+template <int D, int DT, int DG = D>
 static int launch_decode(const DecParams& p, bool opts, hipStream_t st) {
   const long long nwg = (long long)p.B * p.Hkv * p.num_splits;
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if (p.k_new && p.T > 1) {
     const long long rows = (long long)p.B * p.T * p.Hkv;
-    hipLaunchKernelGGL((decode_append_kernel<D, DT>), dim3((int)((rows + 3) / 4)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((decode_append_kernel<DG, DT>), dim3((int)((rows + 3) / 4)), dim3(256), 0, st, p);
   }
   prof_before(FA_KERNEL_DECODE_SPLIT, st);
-  if (opts) hipLaunchKernelGGL((decode_split_kernel<D, DT, true>), dim3((int)nwg), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((decode_split_kernel<D, DT, false>), dim3((int)nwg), dim3(256), 0, st, p);
+  if (opts) hipLaunchKernelGGL((decode_split_kernel<D, DT, true, DG>), dim3((int)nwg), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((decode_split_kernel<D, DT, false, DG>), dim3((int)nwg), dim3(256), 0, st, p);
   prof_after(FA_KERNEL_DECODE_SPLIT, st);
   if (p.num_splits > 1) {
     prof_before(FA_KERNEL_DECODE_COMBINE, st);
-    hipLaunchKernelGGL((decode_combine_kernel<D, DT>), dim3(p.B * p.Hq * p.T), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_combine_kernel<DG, DT>), dim3(p.B * p.Hq * p.T), dim3(64), 0, st, p);
     prof_after(FA_KERNEL_DECODE_COMBINE, st);
   }
   return launch_status();
@@ -636,8 +660,9 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   if (rotary_cos && (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > D)) return FA_ERR_INVALID_ARG;
   if (rotary_cos && (!aligned4(rotary_cos) || !aligned4(rotary_sin))) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
-  // the four-stage K register ring does not fit D = 256; D = 32 is not built
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // D = 256: the four-stage K register ring does not fit beside the query
+  // (high and low parts) and O registers
+  if (D == 256) return FA_ERR_UNSUPPORTED;
   // the G * Sq_new new queries of a K/V head are the 32 MFMA columns
   if ((long long)(Hq / Hkv) * Sq_new > 32) return FA_ERR_UNSUPPORTED;
   if (num_splits == 0) num_splits = auto_splits(B, Hkv, max_blocks_per_seq);
@@ -679,8 +704,12 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   // left window, softcap or ALiBi changes the scores
   const bool opts = softcap > 0.0f || alibi_slopes != nullptr || window_left >= 0;
   hipStream_t s = (hipStream_t)stream;
-  if (D == 128) {
-    return dtype == FA_DTYPE_BF16 ? launch_decode<128, DT_BF16>(p, opts, s) : launch_decode<128, DT_F16>(p, opts, s);
+  const bool bf = dtype == FA_DTYPE_BF16;
+  switch (D) {
+    case 32: return bf ? launch_decode<32, DT_BF16>(p, opts, s) : launch_decode<32, DT_F16>(p, opts, s);
+    case 64: return bf ? launch_decode<64, DT_BF16>(p, opts, s) : launch_decode<64, DT_F16>(p, opts, s);
+    case 96: return bf ? launch_decode<128, DT_BF16, 96>(p, opts, s) : launch_decode<128, DT_F16, 96>(p, opts, s);
+    case 128: return bf ? launch_decode<128, DT_BF16>(p, opts, s) : launch_decode<128, DT_F16>(p, opts, s);
+    default: return FA_ERR_UNSUPPORTED;
   }
-  return dtype == FA_DTYPE_BF16 ? launch_decode<64, DT_BF16>(p, opts, s) : launch_decode<64, DT_F16>(p, opts, s);
 }

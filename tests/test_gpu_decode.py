@@ -231,3 +231,16 @@ def test_multi_token_decode(case):
         _check_cache(c, ref, kc, vc)
     else:
         assert torch.equal(kc.cpu(), c.k_cache) and torch.equal(vc.cpu(), c.v_cache)
+
+
+# Head dims 32 and 96 (96 runs padded on the 128-wide kernel).
+@pytest.mark.parametrize("D,rd", [(32, 32), (96, 96), (96, 32)])
+@pytest.mark.parametrize("num_splits,T", [(1, 1), (3, 1), (2, 3)])
+def test_decode_head_dims(D, rd, num_splits, T):
+    c = decode_case(B=3, Hq=8, Hkv=2, D=D, page=64, seqlens=[300, 63, 1], seed=60 + D, rotary_dim=rd, sq_new=T)
+    say("decode head dim", D, rd, num_splits, T)
+    out, lse, kc, vc = _run(c, num_splits, causal=True)
+    ref = _oracle(c, causal=True)
+    assert_out(out, ref["out"], c.q.dtype)
+    assert_lse(lse, ref["lse"])
+    _check_cache(c, ref, kc, vc)

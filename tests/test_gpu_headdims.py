@@ -99,7 +99,7 @@ def test_dropout_and_packed(D):
 
 
 def test_decode_rejects_unbuilt_head_dims():
-    for D in (32, 96, 256):
+    for D in (256,):
         q = torch.zeros(1, 1, 4, D, dtype=torch.bfloat16, device=DEV)
         kc = torch.zeros(1, 64, 4, D, dtype=torch.bfloat16, device=DEV)
         sl = torch.ones(1, dtype=torch.int32, device=DEV)
