@@ -141,7 +141,7 @@ def run_fwdbwd(args, torch, fa):
                         "tflops": round(fl / ms / 1e9, 1)})
     # dropout (p = 0.1) on the long sequences, reported beside the headline
     drop = []
-    for t in cases:
+    for t in ([] if args.no_extras else cases):
         if t["S"] < 4096:
             continue
         for causal in (False, True):
@@ -164,7 +164,7 @@ def run_fwdbwd(args, torch, fa):
                          "tflops": round(fl / ms / 1e9, 1)})
     # other head dims at hidden 2048 (H = 2048 / D), S = 4K, B = 4
     by_d = []
-    for Dh in (32, 64, 96, 256):
+    for Dh in (() if args.no_extras else (32, 64, 96, 256)):
         Hh = 2048 // Dh if 2048 % Dh == 0 else 24  # D = 96: 24 heads (hidden 2304)
         g = torch.Generator().manual_seed(2)
         mk = lambda: torch.randn(4, 4096, Hh, Dh, generator=g).to(torch.bfloat16).to(dev)
@@ -190,7 +190,7 @@ def run_fwdbwd(args, torch, fa):
     # forward only: bf16 vs fp8 (q/k/v e4m3 with per-(batch, head) factors;
     # the fp8 -> bf16 copy of V is inside the timed call)
     fp8 = []
-    for t in cases:
+    for t in ([] if args.no_extras else cases):
         if t["S"] < 4096:
             continue
         amax = lambda x: (x.float().abs().amax(dim=(1, 3)) / 240.0).contiguous()  # (B, H)
@@ -424,6 +424,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--fwdbwd-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dropout, head-dim and fp8 side measurements (profiling runs)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="write profiles/traffic.json from four rocprofv3 --pmc output directories")
     args = ap.parse_args()
