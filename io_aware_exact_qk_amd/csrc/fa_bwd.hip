@@ -251,13 +251,46 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
         int cls = classify(r0 + off, min(r0 + 31, Sq - 1) + off, kw0, kw0 + 31, Sk, mask);
         if (cls == 0) continue;
         if (r0 + 31 >= Sq) cls = 1;  // rows past the end hold a copy of the last row
-        // S = Q K^T and dP = dO V^T: rows = 32 queries, columns = this wave's keys
+        // S = Q K^T and dP = dO V^T: rows = 32 queries, columns = this wave's
+        // keys.  Every phase below is one explicitly ordered block
+        // (sched_barrier after every MFMA) whose LDS operands run in rings a
+        // few MFMAs ahead of their use, so no MFMA waits for the full LDS
+        // latency of its own operand.
+        const char* qr = qt + (32 * rb) * (D * 2);
+        const char* dr = dot + (32 * rb) * (D * 2);
+        constexpr int R1 = KC > 2 ? 2 : 1;  // chunk steps in flight ahead
+        constexpr int N2 = 4 * DB;          // dV and dK MFMAs
+        constexpr int R2 = 3;               // transposed operands in flight
+        auto op2 = [&](int i) -> u32x4 {
+          const int mk = i / (2 * DB), d = (i >> 1) % DB;
+          return lds_At<D>(((i & 1) ? qt : dot) + (32 * rb + 16 * mk) * (D * 2), tbv, d);
+        };
         f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          u32x4 qa[R1 + 1], oa[R1 + 1], va[R1 + 1];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          s = mfma32<DT>(lds_nat(qt + (32 * rb) * (D * 2), nbv, c), kreg[c], s);
-          dp = mfma32<DT>(lds_nat(dot + (32 * rb) * (D * 2), nbv, c), lds_nat(vw, nbv, c), dp);
+          for (int k = 0; k < R1; ++k) {
+            qa[k] = lds_nat(qr, nbv, k);
+            oa[k] = lds_nat(dr, nbv, k);
+            va[k] = lds_nat(vw, nbv, k);
+          }
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            if (c + R1 < KC) {
+              const int sl = (c + R1) % (R1 + 1);
+              qa[sl] = lds_nat(qr, nbv, c + R1);
+              oa[sl] = lds_nat(dr, nbv, c + R1);
+              va[sl] = lds_nat(vw, nbv, c + R1);
+            }
+            s = mfma32<DT>(qa[c % (R1 + 1)], kreg[c], s);
+            dp = mfma32<DT>(oa[c % (R1 + 1)], va[c % (R1 + 1)], dp);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+        // the first dV / dK operands load under the element-wise work
+        u32x4 r2[R2];
+#pragma unroll
+        for (int i = 0; i < R2; ++i) r2[i] = op2(i);
         // logits, mask (rows past Sq hold a copy of the last row), P and dS
         if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
@@ -300,15 +333,20 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
           }
         }
         // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over the 32 query rows)
+        u32x4 pb[2], sb2[2];
 #pragma unroll
         for (int mk = 0; mk < 2; ++mk) {
-          const u32x4 pb = pack_frag_half<DT>(s, mk);
-          const u32x4 sb2 = pack_frag_half<DT>(dp, mk);
+          pb[mk] = pack_frag_half<DT>(s, mk);
+          sb2[mk] = pack_frag_half<DT>(dp, mk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            dvacc[d] = mfma32<DT>(lds_At<D>(dot + (32 * rb + 16 * mk) * (D * 2), tbv, d), pb, dvacc[d]);
-            dkacc[d] = mfma32<DT>(lds_At<D>(qt + (32 * rb + 16 * mk) * (D * 2), tbv, d), sb2, dkacc[d]);
-          }
+        for (int i = 0; i < N2; ++i) {
+          const int mk = i / (2 * DB), d = (i >> 1) % DB;
+          if (i & 1) dkacc[d] = mfma32<DT>(r2[i % R2], sb2[mk], dkacc[d]);
+          else dvacc[d] = mfma32<DT>(r2[i % R2], pb[mk], dvacc[d]);
+          if (i + R2 < N2) r2[i % R2] = op2(i + R2);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       dma_wait();
@@ -432,54 +470,79 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
       const int j0 = t * BC;
       // keys past the end hold a copy of the last key: classify marks such tiles partial
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
-      // The tile body is written out twice, without and with the mask, so the
-      // common unmasked case is one basic block in which the scheduler can
-      // overlap one 32-key half's exponentials with the other half's MFMAs:
-      // S/dP(0), S/dP(1), P/dS(0), dQ(0), P/dS(1), dQ(1).
+      // The tile body is written out twice, without and with the mask.  Both
+      // are one explicitly ordered block (sched_barrier after every MFMA):
+      //   S/dP of half 0, then S/dP of half 1 with the element-wise work of
+      //   half 0 (P, dS) spread over its MFMAs, then dQ of half 0 with the
+      //   element-wise work of half 1 spread over it, then dQ of half 1.
+      // LDS operands run in rings a few MFMAs ahead of their use, so no MFMA
+      // waits for the full LDS latency of its own operand.
       auto body = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
+        constexpr int NA = 4 * KC;  // S and dP MFMAs of both halves
+        constexpr int NB = 4 * DB;  // dQ MFMAs of both halves
+        constexpr int RA = 4;       // natural-order operands in flight
+        constexpr int RB = 3;       // transposed operands in flight
+        auto op_a = [&](int i) -> u32x4 {
+          const int kb = i / (2 * KC), c = (i >> 1) % KC;
+          return lds_nat(((i & 1) ? vt : kt) + (kb * 32) * (D * 2), nbv, c);
+        };
+        auto op_b = [&](int i) -> u32x4 { return lds_At<D>(kt + (16 * (i / DB)) * (D * 2), tbv, i % DB); };
         f32x16 s[2], dp[2];
+        uint32_t kx[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           s[kb] = f32x16{};
           dp[kb] = f32x16{};
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            s[kb] = mfma32<DT>(lds_nat(kt + (kb * 32) * (D * 2), nbv, c), qreg[c], s[kb]);
-            dp[kb] = mfma32<DT>(lds_nat(vt + (kb * 32) * (D * 2), nbv, c), doreg[c], dp[kb]);
-          }
+          if constexpr (DROP) drop_words<false>(p.drop, (uint32_t)(b * p.Hq + h), my_row, j0 + 32 * kb, lane, kx[kb]);
         }
-        // all S/dP MFMAs are issued before any exponential: the matrix core
-        // works through the second half while the VALU handles the first
-        __builtin_amdgcn_sched_barrier(0);
+        // element i of half kb: logit, mask (keys past Sk hold a copy of the
+        // last key), P, and dS in place of dP
+        auto elem = [&](int kb, int i) {
+          const int j = j0 + 32 * kb + frag_row(i, g);
+          float x = s[kb][i];
+          if constexpr (SOFTCAP || ALIBI) x = logit2<SOFTCAP, ALIBI>(x, ip, j, p, slope_log2);
+          if constexpr (MASKED) x = (row_ok & visible(ip, j, Sk, mask)) ? x : -INFINITY;
+          const float pv = fast_exp2(fmaf(x, fs, -lse2));
+          float dpv = dp[kb][i];
+          if constexpr (DROP) dpv = drop_keep(kx[kb], i, p.drop.t) ? dpv * p.drop.scale : 0.0f;
+          float ds = pv * (dpv - dv_row);
+          if constexpr (SOFTCAP) ds = softcap_grad<ALIBI>(ds, pv, x, ip, j, p, slope_log2);
+          dp[kb][i] = ds;
+        };
+        u32x4 db[4];
+        u32x4 ra[RA], rb[RB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint32_t kx[4];
-          if constexpr (DROP) drop_words<false>(p.drop, (uint32_t)(b * p.Hq + h), my_row, j0 + 32 * kb, lane, kx);
-          // logits, mask (keys past Sk hold a copy of the last key), P and dS
+        for (int i = 0; i < RA; ++i) ra[i] = op_a(i);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + 32 * kb + frag_row(i, g);
-            float x = s[kb][i];
-            if constexpr (SOFTCAP || ALIBI) x = logit2<SOFTCAP, ALIBI>(x, ip, j, p, slope_log2);
-            if constexpr (MASKED) x = (row_ok & visible(ip, j, Sk, mask)) ? x : -INFINITY;
-            const float pv = fast_exp2(fmaf(x, fs, -lse2));
-            float dpv = dp[kb][i];
-            if constexpr (DROP) dpv = drop_keep(kx, i, p.drop.t) ? dpv * p.drop.scale : 0.0f;
-            float ds = pv * (dpv - dv_row);
-            if constexpr (SOFTCAP) ds = softcap_grad<ALIBI>(ds, pv, x, ip, j, p, slope_log2);
-            dp[kb][i] = ds;
+        for (int i = 0; i < NA; ++i) {
+          const int kb = i / (2 * KC), c = (i >> 1) % KC;
+          if (i & 1) dp[kb] = mfma32<DT>(ra[i % RA], doreg[c], dp[kb]);
+          else s[kb] = mfma32<DT>(ra[i % RA], qreg[c], s[kb]);
+          if (i + RA < NA) ra[i % RA] = op_a(i + RA);
+          else if (i + RA - NA < RB) rb[i + RA - NA] = op_b(i + RA - NA);
+          if (kb == 1) {
+            const int jj = i - 2 * KC;
+#pragma unroll
+            for (int e = 16 * jj / (2 * KC); e < 16 * (jj + 1) / (2 * KC); ++e) elem(0, e);
+            if (16 * (jj + 1) / (2 * KC) >= 8 && 16 * jj / (2 * KC) < 8) db[0] = pack_frag_half<DT>(dp[0], 0);
           }
-          // dQ^T += K^T dS^T over this half's 32 keys
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        db[1] = pack_frag_half<DT>(dp[0], 1);
 #pragma unroll
-          for (int mh = 0; mh < 2; ++mh) {
-            const int mk = 2 * kb + mh;
-            const u32x4 db = pack_frag_half<DT>(dp[kb], mh);
+        for (int i = 0; i < NB; ++i) {
+          const int mk = i / DB, d = i % DB;
+          dqacc[d] = mfma32<DT>(rb[i % RB], db[mk], dqacc[d]);
+          if (i + RB < NB) rb[i % RB] = op_b(i + RB);
+          if (mk < 2) {
+            const int jj = i;
 #pragma unroll
-            for (int d = 0; d < DB; ++d) {
-              dqacc[d] = mfma32<DT>(lds_At<D>(kt + (16 * mk) * (D * 2), tbv, d), db, dqacc[d]);
-            }
+            for (int e = 16 * jj / (2 * DB); e < 16 * (jj + 1) / (2 * DB); ++e) elem(1, e);
+            if (16 * (jj + 1) / (2 * DB) >= 8 && 16 * jj / (2 * DB) < 8) db[2] = pack_frag_half<DT>(dp[1], 0);
+            if (jj == 2 * DB - 1) db[3] = pack_frag_half<DT>(dp[1], 1);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       };
       if (cls == 2) body(std::false_type{});
