@@ -11,11 +11,11 @@
 //
 // Three kernels, none with atomics, so every result is bitwise reproducible
 // (the pages' deterministic=True option is therefore always satisfied):
-//   1. row terms  delta_i = sum_d dO_id O_id  and  LSE_i log2(e)  (float32);
-//   2. dK/dV: one work-group per 128 keys of one K/V head; each wave keeps 32
-//      keys' K and V rows in VGPRs and walks every query head of its group and
-//      every query tile of 64 rows in a fixed order, with Q and dO tiles
-//      copied into LDS by DMA.  S = Q K^T puts one key per lane, so
+//   1. row terms  -delta_i = -sum_d dO_id O_id  and  LSE_i log2(e)  (float32);
+//   2. dK/dV: one work-group per 256 keys of one K/V head; each wave keeps 32
+//      keys' K rows in VGPRs (their V rows sit in LDS) and walks every query
+//      head of its group and every query tile of 64 rows in a fixed order,
+//      with Q and dO tiles copied into LDS by DMA.  S = Q K^T puts one key per lane, so
 //      dV^T += dO^T P and dK^T += Q^T dS take P / dS straight from the
 //      accumulators;
 //   3. dQ: one work-group per 128 query rows of one query head (same layout
@@ -37,7 +37,7 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float* dvec;  // workspace: row term delta, same layout as lse
+  float* dvec;  // workspace: row term -delta, same layout as lse
   float* lse2;  // workspace: lse * log2(e), same layout as lse
   uint16_t* dq;
   uint16_t* dk;
@@ -90,8 +90,9 @@ __device__ __forceinline__ int64_t row_index(const BwdParams& p, int b, int h, i
 
 // ------------------------------------------------------------ row term ----
 // One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).  Writes
-// delta = sum_d dO O and the forward's LSE in log2 units, the two per-row
-// values the recompute kernels need.
+// -delta = -sum_d dO O and the forward's LSE in log2 units, the two per-row
+// values the recompute kernels need (the negated delta is the starting value
+// of the dK/dV kernel's dP accumulator).
 // A head's D / 8 chunks go to NCH lanes, rounded up to a power of two for the
 // shuffle reduction (D = 96: 16 lanes, 12 of them loading).
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
       const int b = token / p.Sq, i = token % p.Sq;
       idx = ((int64_t)b * p.Hq + h) * p.Sq + i;
     }
-    p.dvec[idx] = acc;
+    p.dvec[idx] = -acc;
     p.lse2[idx] = p.lse[idx] * kLog2e;
   }
 }
@@ -163,14 +164,19 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   constexpr int NW = DkdvShape<D>::NW, BC = 32 * NW, BR = DkdvShape<D>::BR;
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int TILE = BR * D * 2;
-  // LSE and delta rows: 64 floats each whatever BR is (one 4-byte DMA per lane)
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
-  // V rows of the work-group's keys (B operand of dP = dO V^T), and two stage
-  // buffers, distinct arrays so that reads of one are never ordered behind
-  // the DMA into the other
-  __shared__ __attribute__((aligned(1024))) char vsm[BC * D * 2];
+  // A stage: LSE and delta rows (64 floats each whatever BR is, one 4-byte
+  // DMA per lane), then the Q and dO tiles.
+  constexpr int ROWT = 2 * 64 * 4;
+  constexpr int STAGE = ROWT + 2 * TILE;
+  // Two stage buffers and the V rows of the work-group's keys (B operand of
+  // dP = dO V^T) in two halves: distinct arrays, so that reads of one are
+  // never ordered behind the DMA into another.  Each V half is smaller than a
+  // stage, so the stages are placed first and every stage tile base stays
+  // below 64 KB, within the immediate offset of the LDS reads.
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char vsm0[BC / 2 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vsm1[BC / 2 * D * 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -197,12 +203,14 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
     const bool in = DG == D || (2 * c + g) * 8 < DG;
     kreg[c] = (key_ok && in) ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
-  zero_pad<D, BC, DG>(vsm, tid, 64 * NW);
-  zero_pad<D, BR, DG>(sm0, tid, 64 * NW);
-  zero_pad<D, BR, DG>(sm0 + TILE, tid, 64 * NW);
-  zero_pad<D, BR, DG>(sm1, tid, 64 * NW);
-  zero_pad<D, BR, DG>(sm1 + TILE, tid, 64 * NW);
-  const char* vw = vsm + (32 * w) * (D * 2);  // this wave's 32 V rows
+  zero_pad<D, BC / 2, DG>(vsm0, tid, 64 * NW);
+  zero_pad<D, BC / 2, DG>(vsm1, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm0 + ROWT, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm0 + ROWT + TILE, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm1 + ROWT, tid, 64 * NW);
+  zero_pad<D, BR, DG>(sm1 + ROWT + TILE, tid, 64 * NW);
+  // this wave's 32 V rows
+  const char* vw = (w < NW / 2 ? vsm0 : vsm1) + (32 * (w % (NW / 2))) * (D * 2);
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
@@ -223,12 +231,12 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
       const int i0 = (t_lo + n % nt) * BR;
       const int64_t hoff = (int64_t)sb.q_start * p.q_rstride + (int64_t)hq * DG;
       const int64_t ooff = (int64_t)sb.q_start * p.o_rstride + (int64_t)hq * DG;
-      dma_tile<D, BR, NW, true, DG>(st, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
-      dma_tile<D, BR, NW, true, DG>(st + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW, true, DG>(st + ROWT, p.q + hoff, p.q_rstride, i0, Sq, w, lane);
+      dma_tile<D, BR, NW, true, DG>(st + ROWT + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
         const int i = min(i0 + lane, Sq - 1);
-        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + 2 * TILE + w * 64 * 4);
+        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + w * 64 * 4);
       }
     };
 
@@ -238,9 +246,9 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const int hq = hk * p.g + n / nt;
       const int i0 = (t_lo + n % nt) * BR;
-      const char* qt = st;
-      const char* dot = st + TILE;
-      const float* lse2 = reinterpret_cast<const float*>(st + 2 * TILE);
+      const char* qt = st + ROWT;
+      const char* dot = st + ROWT + TILE;
+      const float* lse2 = reinterpret_cast<const float*>(st);
       const float* dvs = lse2 + 64;
       const float slope_log2 = ALIBI ? p.alibi[hq] * kLog2e : 0.0f;
       const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
@@ -265,7 +273,17 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
           const int mk = i / (2 * DB), d = (i >> 1) % DB;
           return lds_At<D>(((i & 1) ? qt : dot) + (32 * rb + 16 * mk) * (D * 2), tbv, d);
         };
+        // dP accumulates onto -delta (stored negated), so it leaves the MFMAs
+        // as dP - delta; with dropout the keep mask acts on dP alone
         f32x16 s = f32x16{}, dp = f32x16{};
+        if constexpr (!DROP) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvs + 32 * rb + 8 * qd + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * qd + e] = d4[e];
+          }
+        }
         {
           u32x4 qa[R1 + 1], oa[R1 + 1], va[R1 + 1];
 #pragma unroll
@@ -313,7 +331,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 32 * rb + 8 * qd + 4 * g);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvs + 32 * rb + 8 * qd + 4 * g);
+          f32x4 d4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(dvs + 32 * rb + 8 * qd + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int ii = 4 * qd + e;
@@ -322,9 +341,9 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
             float dpv = dp[ii];
             if constexpr (DROP) {
               keep = drop_keep(kx, ii, p.drop.t);
-              dpv = keep ? dpv * p.drop.scale : 0.0f;
+              dpv = (keep ? dpv * p.drop.scale : 0.0f) + d4[e];
             }
-            float ds = pv * (dpv - d4[e]);
+            float ds = pv * dpv;
             if constexpr (SOFTCAP) {
               ds = softcap_grad<ALIBI>(ds, pv, s[ii], r0 + frag_row(ii, g) + off, my_key, p, slope_log2);
             }
@@ -354,8 +373,9 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
     };
 
     // V rows past Sk hold a copy of the last row; their keys are masked
-    dma_tile<D, BC, NW, true, DG>(vsm, p.v + (int64_t)sb.k_start * p.k_rstride + hk * DG, p.k_rstride, k0, Sk,
-                                  w, lane);
+    const uint16_t* vsrc = p.v + (int64_t)sb.k_start * p.k_rstride + hk * DG;
+    dma_tile<D, BC / 2, NW, true, DG>(vsm0, vsrc, p.k_rstride, k0, Sk, w, lane);
+    dma_tile<D, BC / 2, NW, true, DG>(vsm1, vsrc, p.k_rstride, k0 + BC / 2, Sk, w, lane);
     issue(0, sm0);
     dma_wait();
     __syncthreads();
@@ -436,11 +456,11 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   zero_pad<D, BC, DG>(sm0 + TILE, tid, 256);
   zero_pad<D, BC, DG>(sm1, tid, 256);
   zero_pad<D, BC, DG>(sm1 + TILE, tid, 256);
-  float lse2 = INFINITY, dv_row = 0.0f;  // rows past the end: P = 0
+  float lse2 = INFINITY, ndelta = 0.0f;  // rows past the end: P = 0
   if (row_ok) {
     const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
     lse2 = p.lse2[ri];
-    dv_row = p.dvec[ri];
+    ndelta = p.dvec[ri];
   }
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
   const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
@@ -506,7 +526,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
           const float pv = fast_exp2(fmaf(x, fs, -lse2));
           float dpv = dp[kb][i];
           if constexpr (DROP) dpv = drop_keep(kx[kb], i, p.drop.t) ? dpv * p.drop.scale : 0.0f;
-          float ds = pv * (dpv - dv_row);
+          float ds = pv * (dpv + ndelta);
           if constexpr (SOFTCAP) ds = softcap_grad<ALIBI>(ds, pv, x, ip, j, p, slope_log2);
           dp[kb][i] = ds;
         };

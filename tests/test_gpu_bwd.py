@@ -45,8 +45,15 @@ def test_small_cases(case):
     say("bwd small", case)
     dq, dk, dv = _run(c)
     gq, gk, gv = attention_bwd(c.q, c.k, c.v, c.dout, c.scale, causal, window, softcap, c.alibi_slopes)
-    assert_grad(dq, gq, "dq")
-    assert_grad(dk, gk, "dk")
+    if Sk == 1:
+        # one key: P = 1 and dS = P (dP - delta) cancels exactly, so dq = dk = 0
+        # and the relative bound degenerates; float32 leaves only the rounding
+        # residue of dP - delta (dP from the MFMA, delta = dO . O summed apart)
+        assert np.abs(dq.float().cpu().numpy()).max() <= 1e-5
+        assert np.abs(dk.float().cpu().numpy()).max() <= 1e-5
+    else:
+        assert_grad(dq, gq, "dq")
+        assert_grad(dk, gk, "dk")
     assert_grad(dv, gv, "dv")
 
 
