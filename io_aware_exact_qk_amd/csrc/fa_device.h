@@ -45,7 +45,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Online softmax: how far (log2 units) a row max may exceed the exponent
 // reference before the accumulators are rescaled.
 constexpr float kRescaleSlack = 8.0f;
-constexpr float kRescaleLimit = 256.0f;  // 2^kRescaleSlack
 
 // ---------------------------------------------------------------- MFMA ----
 // 32 x 32 x 64 product of fp8 (OCP e4m3) operands, float32 accumulate: each

@@ -206,8 +206,9 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     };
 
     // Logits of tile t in the log2 domain (up to the folded scale fs), masked
-    // entries at -inf (keys past Sk hold a copy of the last key).
-    auto logits = [&](int t, f32x16 (&sa)[2]) {
+    // entries at -inf (keys past Sk hold a copy of the last key), then the
+    // lazy online-softmax update of the exponent reference.  Returns m_use.
+    auto prep = [&](int t, f32x16 (&sa)[2]) -> float {
       const int j0 = t * BC;
       if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
@@ -234,14 +235,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
           }
         }
       }
-    };
-
-    // Lazy online-softmax update of the exponent reference from the tile
-    // maximum: m_run moves only when the tile max exceeds it by more than
-    // kRescaleSlack; until then p <= 2^kRescaleSlack, which the float32 sums
-    // and the 16-bit P operand carry without loss, and the rescale of O
-    // (64 multiplies per lane) is skipped.  Returns the reference to use.
-    auto update_max = [&](const f32x16 (&sa)[2]) -> float {
+      // The exponent reference m_run moves only when the tile max exceeds it
+      // by more than kRescaleSlack; until then p <= 2^kRescaleSlack, which the
+      // float32 sums and the 16-bit P operand carry without loss, and the
+      // rescale of O (64 multiplies per lane) is skipped.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -257,11 +254,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
         m_run = m_new;
       }
       return (m_run == -INFINITY) ? 0.0f : m_run;
-    };
-
-    auto prep = [&](int t, f32x16 (&sa)[2]) -> float {
-      logits(t, sa);
-      return update_max(sa);
     };
 
     // Dropout keep words of tile t (two 32-key halves).
@@ -309,7 +301,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     // down next to its MFMA, which would expose the whole LDS latency on
     // every MFMA.
     auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, f32x16 (&sc)[2],
-                     f32x16 (&sn)[2], float m_use) {
+                     f32x16 (&sn)[2], float m_use, const uint32_t (&kw)[2][4]) {
       constexpr int NS = 2 * KC;    // S MFMAs per tile
       constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
       u32x4 kr[4];
@@ -319,7 +311,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       sn[1] = f32x16{};
       float lsum = 0.0f;
       u32x4 pb[4];
-      float pt[8];  // P of the 16-bit pair group being packed
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int kb = i / KC, c = i % KC;
@@ -330,32 +321,13 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
           const int idx = i * EPS + e;
           const float pv = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
           lsum += pv;
-          pt[idx & 7] = pv;
-          if ((idx & 7) == 7) {
-            const int mk = idx >> 3;
-            pb[mk] = u32x4{pack2<DT>(pt[0], pt[1]), pack2<DT>(pt[2], pt[3]), pack2<DT>(pt[4], pt[5]),
-                           pack2<DT>(pt[6], pt[7])};
-          }
+          sc[idx >> 4][idx & 15] = (DROP && !drop_keep(kw[idx >> 4], idx & 15, p.drop.t)) ? 0.0f : pv;
+        }
+        if (((i + 1) * EPS) % 8 == 0) {
+          const int mk = (i + 1) * EPS / 8 - 1;
+          pb[mk] = pack_frag_half<DT>(sc[mk >> 1], mk & 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      // Every p of this lane is at most its sum, so a lane sum within
-      // 2^kRescaleSlack proves the reference still valid without the tile
-      // maximum.  Otherwise (rare: the running maximum moved up) take the
-      // maximum, rescale, and redo the exponentials from the kept logits.
-      if (__any(lsum > kRescaleLimit)) {
-        const float mu = update_max(sc);
-        lsum = 0.0f;
-#pragma unroll
-        for (int idx = 0; idx < 32; ++idx) {
-          const float pv = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -mu));
-          lsum += pv;
-          pt[idx & 7] = pv;
-          if ((idx & 7) == 7) {
-            pb[idx >> 3] = u32x4{pack2<DT>(pt[0], pt[1]), pack2<DT>(pt[2], pt[3]), pack2<DT>(pt[4], pt[5]),
-                                 pack2<DT>(pt[6], pt[7])};
-          }
-        }
       }
       l_run += lsum;
       constexpr int NP = 4 * DB;  // P V MFMAs per tile
@@ -381,11 +353,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       if (t + 2 < t_hi) dma_k(t + 2, kdst);
       dma_v(t + 1, vdst);
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
-      logits(t, sc);
-      // the tile maximum is needed only while a row has no reference yet
-      const float m_use = __any(row_ok & (m_run == -INFINITY)) ? update_max(sc)
-                                                               : (m_run == -INFINITY ? 0.0f : m_run);
-      fused(kn, vt, nbv, tbv, sc, sn, m_use);
+      uint32_t kw[2][4];
+      keepw(t, kw);
+      const float m_use = prep(t, sc);
+      fused(kn, vt, nbv, tbv, sc, sn, m_use, kw);
       dma_wait();
       __syncthreads();
     };
