@@ -98,8 +98,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace fa_bwd needs (host-only, pure): two float32 row arrays
- * (B, Hq, Sq) -- the row term sum_d dO*O and the LSE in log2 units -- each
- * padded to 256 bytes. */
+ * (B, Hq, Sq) -- the negated row term -sum_d dO*O and the LSE in log2
+ * units -- each padded to 256 bytes. */
 size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int deterministic);
 
 /*
