@@ -235,8 +235,8 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
       dma_tile<D, BR, NW, true, DG>(st + ROWT + TILE, p.dout + ooff, p.o_rstride, i0, Sq, w, lane);
       if (w < 2) {
         const float* src = (w == 0) ? p.lse2 : p.dvec;
-        const int i = min(i0 + lane, Sq - 1);
-        dma4(src + row_index(p, b, hq, sb.q_start, Sq, i), st + w * 64 * 4);
+        const int i = min(i0 + lane, Sq - 1);  // i0 < Sq, so i - i0 >= 0
+        dma4(make_rsrc(src + row_index(p, b, hq, sb.q_start, Sq, i0)), (uint32_t)(i - i0) * 4u, st + w * 64 * 4);
       }
     };
 
@@ -423,7 +423,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   __shared__ __attribute__((aligned(1024))) char sm0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char sm1[2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index stays a per-lane value here: declared uniform (readfirstlane)
+  // it changes register allocation enough to spill about 80 VGPRs
+  const int w = tid >> 6;
   const int g = lane >> 5, r = lane & 31;
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);

@@ -243,19 +243,34 @@ __device__ __forceinline__ u32x4 lds_At(const char* tile, uint32_t tb, int d) {
 }
 
 // ----------------------------------------------------- global -> LDS DMA --
-// global_load_lds_dwordx4: every lane fetches 16 bytes from its own global
-// address and the hardware writes lane l's bytes to LDS at base + 16 * l, so
-// one instruction fills one contiguous 1 KB block without passing through
-// VGPRs.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* src, char* lds_block) {
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 16, 0, 0);
+// buffer_load_dword{,x4} ... lds: every lane fetches 4 or 16 bytes from
+// base + soffset + its own voffset and the hardware writes lane l's bytes to
+// LDS at lds_block + size * l, so one x4 instruction fills one contiguous 1 KB
+// block without passing through VGPRs.  Completion is tracked by vmcnt.
+//
+// The buffer (MUBUF) form is used rather than global_load_lds: the compiler
+// models the FLAT-encoded global form as an access that may also count on
+// lgkmcnt, and while one is in flight it turns every LDS-read wait into
+// lgkmcnt(0), which drains the operand rings the kernels keep a few reads
+// ahead.  With the buffer form the waits stay exact (lgkmcnt(n)).
+//
+// The resource covers [base, base + 4 GB) with stride 0 (raw offsets) and the
+// gfx9 default format word; callers keep every offset non-negative and far
+// below 4 GB by rebasing on the first row a call touches.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
 
-// 4-byte variant: lane l's dword lands at base + 4 * l.
-__device__ __forceinline__ void dma4(const void* src, char* lds_block) {
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_block, 4, 0, 0);
+__device__ __forceinline__ void dma16(buf_rsrc r, uint32_t voff, uint32_t soff, char* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_block, 16, voff, soff, 0, 0);
+}
+
+// 4-byte variant: lane l's dword lands at lds_block + 4 * l.
+__device__ __forceinline__ void dma4(buf_rsrc r, uint32_t voff, char* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_block, 4, voff, 0, 0, 0);
 }
 
 // Wait until every DMA (and global load) this wave issued has landed.
@@ -290,24 +305,31 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* base, int64
   if (NBLK < NWAVES && w >= NBLK) return;
   const int rin = lane / NCH, pch = lane % NCH;
   if (FAST && row0 + ROWS <= nrows) {
-    const char* b0 = reinterpret_cast<const char*>(base + (int64_t)row0 * rstride);
+    // resource at row row0; block offsets are wave-uniform (soffset)
+    const buf_rsrc rs = make_rsrc(base + (int64_t)row0 * rstride);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int blk = i * NWAVES + w;
       const int row = blk * RPB + rin;
-      // re-derived per call: hoisting whole 64-bit addresses out of the tile
-      // loop would cost two VGPRs per block
+      // re-derived per call: keeping one offset per block live across the
+      // tile loop would cost a VGPR each
       const uint32_t loff = opaque((uint32_t)(rin * rstride + ((pch ^ (int)swz<D>(row)) << 3)) * 2u);
-      if (DG == D || (pch ^ (int)swz<D>(row)) < DG / 8) dma16(b0 + (int64_t)blk * RPB * rstride * 2 + loff, tile + blk * 1024);
+      const uint32_t soff = (uint32_t)(blk * RPB) * (uint32_t)rstride * 2u;
+      if (DG == D || (pch ^ (int)swz<D>(row)) < DG / 8) dma16(rs, loff, soff, tile + blk * 1024);
     }
   } else {
+    // resource at the first row this call reads (row0 may lie past the last
+    // row, whose copy is then read), so every lane offset is >= 0
+    const int rb = min(row0, nrows - 1);
+    const buf_rsrc rs = make_rsrc(base + (int64_t)rb * rstride);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int blk = i * NWAVES + w;
       const int row = blk * RPB + rin;
       const int lch = pch ^ (int)swz<D>(row);
       const int grow = min(row0 + row, nrows - 1);
-      if (DG == D || lch < DG / 8) dma16(base + (int64_t)grow * rstride + lch * 8, tile + blk * 1024);
+      const uint32_t voff = (uint32_t)((grow - rb) * (int)rstride + lch * 8) * 2u;
+      if (DG == D || lch < DG / 8) dma16(rs, voff, 0u, tile + blk * 1024);
     }
   }
 }
