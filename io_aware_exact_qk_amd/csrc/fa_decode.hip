@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair_max32(mx);
     if constexpr (!OPTS) mx *= p.scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   }
 
   // ---- merge the 4 waves: M = max m_w, each wave scaled by 2^(m_w - M) ----
-  const float l_w = l_run + xor32(l_run);
+  const float l_w = pair_sum32(l_run);
   if (hf == 0) {
     mbuf[w * 32 + r] = m_run;
     lbuf[w * 32 + r] = l_w;

@@ -351,6 +351,20 @@ __device__ __forceinline__ void zero_pad(char* tile, int tid, int nthreads) {
 // ------------------------------------------------------------ wave utils --
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Max / sum of x over lanes l and l ^ 32 with v_permlane32_swap (a VALU
+// exchange, no LDS round trip).  Swapping x with itself leaves the low half
+// of x in both halves of one result and the high half in both halves of the
+// other, so every lane holds the pair {x[l], x[l ^ 32]}; both operations are
+// symmetric, hence bitwise equal to x op xor32(x).
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

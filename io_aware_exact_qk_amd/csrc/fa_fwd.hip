@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[kb][i]);
-      mx = fmaxf(mx, xor32(mx)) * fs;
+      mx = pair_max32(mx) * fs;
       if (__any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum32(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.0f ? (DROP ? p.drop.scale : 1.0f) * (FP8 ? dsv : 1.0f) / l_tot : 0.0f;
     uint16_t* orow = p.o + (int64_t)(q_start + my_row) * p.o_rstride + h * DG;
