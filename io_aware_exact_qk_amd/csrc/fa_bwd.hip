@@ -9,18 +9,19 @@
 //   dS = dZ * (1 - tanh^2(s/c)) with softcap c (else dZ),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, none with atomics, so every result is bitwise reproducible
+// Two kernels, none with atomics, so every result is bitwise reproducible
 // (the pages' deterministic=True option is therefore always satisfied):
-//   1. row terms  -delta_i = -sum_d dO_id O_id  and  LSE_i log2(e)  (float32);
-//   2. dK/dV: one work-group per 256 keys of one K/V head; each wave keeps 32
-//      keys' K rows in VGPRs (their V rows sit in LDS) and walks every query
-//      head of its group and every query tile of 64 rows in a fixed order,
-//      with Q and dO tiles copied into LDS by DMA.  S = Q K^T puts one key per lane, so
-//      dV^T += dO^T P and dK^T += Q^T dS take P / dS straight from the
-//      accumulators;
-//   3. dQ: one work-group per 128 query rows of one query head (same layout
-//      as the forward); it recomputes S^T and dP^T per key tile and
-//      accumulates dQ^T += K^T dS^T.
+//   1. dQ: one work-group per 128 query rows of one query head (same layout
+//      as the forward); it first forms the row terms -delta_i =
+//      -sum_d dO_id O_id and LSE_i log2(e) (float32) of its rows and stores
+//      them for the dK/dV kernel, then recomputes S^T and dP^T per key tile
+//      and accumulates dQ^T += K^T dS^T;
+//   2. dK/dV (launched after dQ on the same stream): one work-group per 256
+//      keys of one K/V head; each wave keeps 32 keys' K rows in VGPRs (their
+//      V rows sit in LDS) and walks every query head of its group and every
+//      query tile of 64 rows in a fixed order, with Q and dO tiles copied
+//      into LDS by DMA.  S = Q K^T puts one key per lane, so dV^T += dO^T P
+//      and dK^T += Q^T dS take P / dS straight from the accumulators.
 // Both recompute kernels fit in 256 VGPRs, so two waves share each SIMD and
 // one wave's exponentials overlap the other's matrix instructions.
 #include <type_traits>
@@ -51,7 +52,6 @@ struct BwdParams {
   const float* alibi;
   int wl, wr;
   int n_tiles, n_heads, n_batch, reverse, balanced;
-  int n_tokens;  // preprocess: number of (token) rows
   DropSpec drop; // DROP kernels only
 };
 
@@ -86,48 +86,6 @@ __device__ __forceinline__ SeqBounds seq_bounds(const BwdParams& p, int b) {
 
 __device__ __forceinline__ int64_t row_index(const BwdParams& p, int b, int h, int q_start, int Sq, int i) {
   return p.cu_q ? (int64_t)h * p.total_q + q_start + i : ((int64_t)b * p.Hq + h) * Sq + i;
-}
-
-// ------------------------------------------------------------ row term ----
-// One 16-lane (D = 128) or 8-lane (D = 64) group per (token, head).  Writes
-// -delta = -sum_d dO O and the forward's LSE in log2 units, the two per-row
-// values the recompute kernels need (the negated delta is the starting value
-// of the dK/dV kernel's dP accumulator).
-// A head's D / 8 chunks go to NCH lanes, rounded up to a power of two for the
-// shuffle reduction (D = 96: 16 lanes, 12 of them loading).
-constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
-
-template <int D, int DT>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int NCH = pow2_at_least(D / 8);
-  const int gid = (blockIdx.x * 256 + threadIdx.x) / NCH;
-  const int ch = threadIdx.x % NCH;
-  const int token = gid / p.Hq, h = gid % p.Hq;
-  const bool ok = token < p.n_tokens;
-  float acc = 0.0f;
-  if (ok && ch < D / 8) {
-    const int64_t base = (int64_t)token * p.o_rstride + h * D + ch * 8;
-    const u32x4 a = gload128(p.o + base);
-    const u32x4 c = gload128(p.dout + base);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(to_f32<DT>((uint16_t)(a[e] & 0xffff)), to_f32<DT>((uint16_t)(c[e] & 0xffff)), acc);
-      acc = fmaf(to_f32<DT>((uint16_t)(a[e] >> 16)), to_f32<DT>((uint16_t)(c[e] >> 16)), acc);
-    }
-  }
-#pragma unroll
-  for (int m = NCH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (ok && ch == 0) {
-    int64_t idx;
-    if (p.cu_q) {
-      idx = (int64_t)h * p.total_q + token;
-    } else {
-      const int b = token / p.Sq, i = token % p.Sq;
-      idx = ((int64_t)b * p.Hq + h) * p.Sq + i;
-    }
-    p.dvec[idx] = -acc;
-    p.lse2[idx] = p.lse[idx] * kLog2e;
-  }
 }
 
 // --------------------------------------------------- logit transform ------
@@ -459,11 +417,33 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   zero_pad<D, BC, DG>(sm0 + TILE, tid, 256);
   zero_pad<D, BC, DG>(sm1, tid, 256);
   zero_pad<D, BC, DG>(sm1 + TILE, tid, 256);
+  // Row terms of this work-group's rows: -delta = -sum_d dO O (lane g sums
+  // its half of the head dim, the two halves meet across lanes l, l ^ 32)
+  // and the LSE in log2 units.  Both are stored for the dK/dV kernel, which
+  // runs after this one on the same stream.
   float lse2 = INFINITY, ndelta = 0.0f;  // rows past the end: P = 0
-  if (row_ok) {
-    const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
-    lse2 = p.lse2[ri];
-    ndelta = p.dvec[ri];
+  {
+    float dacc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const bool in = row_ok && (DG == D || (2 * c + g) * 8 < DG);
+      const u32x4 o4 = in ? gload128(p.o + orow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dacc = fmaf(to_f32<DT>((uint16_t)(o4[e] & 0xffff)), to_f32<DT>((uint16_t)(doreg[c][e] & 0xffff)), dacc);
+        dacc = fmaf(to_f32<DT>((uint16_t)(o4[e] >> 16)), to_f32<DT>((uint16_t)(doreg[c][e] >> 16)), dacc);
+      }
+    }
+    const float dsum = pair_sum32(dacc);
+    if (row_ok) {
+      const int64_t ri = row_index(p, b, h, sb.q_start, Sq, my_row);
+      lse2 = p.lse[ri] * kLog2e;
+      ndelta = -dsum;
+      if (g == 0) {
+        p.dvec[ri] = ndelta;
+        p.lse2[ri] = lse2;
+      }
+    }
   }
   const float slope_log2 = ALIBI ? p.alibi[h] * kLog2e : 0.0f;
   const float fs = (SOFTCAP || ALIBI) ? 1.0f : p.scale_log2;
@@ -604,16 +584,17 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
 // ------------------------------------------------------------- dispatch ---
 template <int D, int DT, bool SC, bool AL, bool DR, int DG>
 static void launch_main(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, hipStream_t st) {
+  // dQ first: it writes the row terms the dK/dV kernel reads
+  if (nwg_q > 0) {
+    prof_before(FA_KERNEL_BWD_DQ, st);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL, DR, DG>), dim3(nwg_q), dim3(256), 0, st, dq);
+    prof_after(FA_KERNEL_BWD_DQ, st);
+  }
   if (nwg_kv > 0) {
     prof_before(FA_KERNEL_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, SC, AL, DR, DG>), dim3(nwg_kv), dim3(64 * DkdvShape<D>::NW), 0, st,
                        dkdv);
     prof_after(FA_KERNEL_BWD_DKDV, st);
-  }
-  if (nwg_q > 0) {
-    prof_before(FA_KERNEL_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, SC, AL, DR, DG>), dim3(nwg_q), dim3(256), 0, st, dq);
-    prof_after(FA_KERNEL_BWD_DQ, st);
   }
 }
 
@@ -626,13 +607,8 @@ static void launch_main_d(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv
 
 // D: the head dim on chip; DG: in memory (DG < D only for D = 96 on 128)
 template <int D, int DT, int DG = D>
-static void launch_all(const BwdParams& pre, int nwg_pre, const BwdParams& dkdv, const BwdParams& dq,
-                       int nwg_kv, int nwg_q, bool sc, bool al, hipStream_t st) {
-  if (nwg_pre > 0) {
-    prof_before(FA_KERNEL_BWD_PREPROCESS, st);
-    hipLaunchKernelGGL((bwd_pre_kernel<DG, DT>), dim3(nwg_pre), dim3(256), 0, st, pre);
-    prof_after(FA_KERNEL_BWD_PREPROCESS, st);
-  }
+static void launch_all(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, int nwg_q, bool sc, bool al,
+                       hipStream_t st) {
   const bool dr = dkdv.drop.t > 0;
   if (sc) {
     if (al) launch_main_d<D, DT, true, true, DG>(dkdv, dq, nwg_kv, nwg_q, dr, st);
@@ -644,12 +620,8 @@ static void launch_all(const BwdParams& pre, int nwg_pre, const BwdParams& dkdv,
 }
 
 static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int max_sk, int nbatch,
-                   int n_tokens, int causal, hipStream_t st) {
+                   int causal, hipStream_t st) {
   if (causal) base.wr = 0;
-  BwdParams pre = base;
-  pre.n_tokens = n_tokens;
-  const long long pre_threads = (long long)n_tokens * base.Hq * pow2_at_least(D / 8);
-  const long long nwg_pre = (pre_threads + 255) / 256;
   BwdParams kv = base;
   const int kv_keys = 32 * (D >= 256 ? DkdvShape<256>::NW : DkdvShape<128>::NW);
   kv.n_tiles = (max_sk + kv_keys - 1) / kv_keys;
@@ -665,30 +637,30 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   dq.balanced = causal ? 1 : 0;
   const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * nbatch;
   const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * nbatch;
-  if (nwg_pre > 0x7fffffffLL || nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const bool sc = base.cap_log2 > 0.0f, al = base.alibi != nullptr;
   const bool bf = dtype == FA_DTYPE_BF16;
-  const int np = (int)nwg_pre, nk = (int)nwg_kv, nq = (int)nwg_q;
+  const int nk = (int)nwg_kv, nq = (int)nwg_q;
   switch (D) {
     case 32:
-      if (bf) launch_all<32, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
-      else launch_all<32, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      if (bf) launch_all<32, DT_BF16>(kv, dq, nk, nq, sc, al, st);
+      else launch_all<32, DT_F16>(kv, dq, nk, nq, sc, al, st);
       break;
     case 64:
-      if (bf) launch_all<64, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
-      else launch_all<64, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      if (bf) launch_all<64, DT_BF16>(kv, dq, nk, nq, sc, al, st);
+      else launch_all<64, DT_F16>(kv, dq, nk, nq, sc, al, st);
       break;
     case 96:  // padded to 128 on chip
-      if (bf) launch_all<128, DT_BF16, 96>(pre, np, kv, dq, nk, nq, sc, al, st);
-      else launch_all<128, DT_F16, 96>(pre, np, kv, dq, nk, nq, sc, al, st);
+      if (bf) launch_all<128, DT_BF16, 96>(kv, dq, nk, nq, sc, al, st);
+      else launch_all<128, DT_F16, 96>(kv, dq, nk, nq, sc, al, st);
       break;
     case 128:
-      if (bf) launch_all<128, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
-      else launch_all<128, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      if (bf) launch_all<128, DT_BF16>(kv, dq, nk, nq, sc, al, st);
+      else launch_all<128, DT_F16>(kv, dq, nk, nq, sc, al, st);
       break;
     default:
-      if (bf) launch_all<256, DT_BF16>(pre, np, kv, dq, nk, nq, sc, al, st);
-      else launch_all<256, DT_F16>(pre, np, kv, dq, nk, nq, sc, al, st);
+      if (bf) launch_all<256, DT_BF16>(kv, dq, nk, nq, sc, al, st);
+      else launch_all<256, DT_F16>(kv, dq, nk, nq, sc, al, st);
       break;
   }
   return launch_status();
@@ -780,7 +752,7 @@ static int bwd_dense(const void* q, const void* k, const void* v, const void* ou
   if (rs.kv) p.k_rstride = rs.kv;
   if (rs.dq) p.dq_rstride = rs.dq;
   if (rs.dkv) p.dkv_rstride = rs.dkv;
-  return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, B * Sq, causal, (hipStream_t)stream);
+  return run_bwd(p, D, dtype, Hkv, Sq, Sk, B, causal, (hipStream_t)stream);
 }
 
 static int bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -808,7 +780,7 @@ static int bwd_varlen(const void* q, const void* k, const void* v, const void* o
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.drop = drop;
-  return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, total_q, causal, (hipStream_t)stream);
+  return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, causal, (hipStream_t)stream);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
