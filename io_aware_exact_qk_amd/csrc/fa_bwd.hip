@@ -467,9 +467,21 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
     };
     // One key tile: `kt` holds K and V of tile t, `nxt` receives tile t + 1.
     auto step = [&](const char* kt, char* nxt, int t) {
-      if (t + 1 < t_hi) issue(t + 1, nxt);
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       const char* vt = kt + TILE;
+      constexpr int RA = 4;  // natural-order operands in flight
+      // operand i of the S / dP phase: K (even i) or V (odd i) rows of key
+      // half i / (2 KC), chunk step (i / 2) % KC
+      auto op_a = [&](int i) -> u32x4 {
+        const int kb = i / (2 * KC), c = (i >> 1) % KC;
+        return lds_nat(((i & 1) ? vt : kt) + (kb * 32) * (D * 2), nbv, c);
+      };
+      // the first operands are read before the copy of the next tile is
+      // issued and the tile is classified, so their LDS latency overlaps that
+      u32x4 ra0[RA];
+#pragma unroll
+      for (int i = 0; i < RA; ++i) ra0[i] = op_a(i);
+      if (t + 1 < t_hi) issue(t + 1, nxt);
       const int j0 = t * BC;
       // keys past the end hold a copy of the last key: classify marks such tiles partial
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
@@ -484,12 +496,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
         constexpr bool MASKED = decltype(masked)::value;
         constexpr int NA = 4 * KC;  // S and dP MFMAs of both halves
         constexpr int NB = 4 * DB;  // dQ MFMAs of both halves
-        constexpr int RA = 4;       // natural-order operands in flight
         constexpr int RB = 3;       // transposed operands in flight
-        auto op_a = [&](int i) -> u32x4 {
-          const int kb = i / (2 * KC), c = (i >> 1) % KC;
-          return lds_nat(((i & 1) ? vt : kt) + (kb * 32) * (D * 2), nbv, c);
-        };
         auto op_b = [&](int i) -> u32x4 { return lds_At<D>(kt + (16 * (i / DB)) * (D * 2), tbv, i % DB); };
         f32x16 s[2], dp[2];
         uint32_t kx[2][4];
@@ -516,7 +523,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
         u32x4 db[4];
         u32x4 ra[RA], rb[RB];
 #pragma unroll
-        for (int i = 0; i < RA; ++i) ra[i] = op_a(i);
+        for (int i = 0; i < RA; ++i) ra[i] = ra0[i];
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
           const int kb = i / (2 * KC), c = (i >> 1) % KC;

@@ -292,30 +292,42 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       }
     };
 
+    // First four K fragments of the next S (LDS tile `kn`).  A step issues
+    // them before its softmax prologue, so their LDS latency is hidden by it.
+    auto k_ring = [&](const char* kn, uint32_t nbv, u32x4 (&kr)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = lds_nat(kn + (i / KC) * 32 * (D * 2), nbv, i % KC);
+    };
+
     // The pipelined block in an explicit instruction order.  S of the next
     // tile: a ring of four K fragments keeps four LDS reads in flight ahead of
     // the MFMA that consumes them, and each MFMA is followed by a slice of the
-    // current tile's softmax (exponentials, row sum, packing of P).  Then
-    // O += P V with a ring of three V^T fragments (six transposed reads) in
-    // flight.  sched_barrier fences keep the scheduler from pulling each read
-    // down next to its MFMA, which would expose the whole LDS latency on
-    // every MFMA.
-    auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, f32x16 (&sc)[2],
-                     f32x16 (&sn)[2], float m_use, const uint32_t (&kw)[2][4]) {
+    // current tile's softmax (exponentials, row sum, packing of P); once the
+    // K ring has nothing left to fetch, its last slots start the first three
+    // V^T fragments.  Then O += P V with a ring of three V^T fragments (six
+    // transposed reads) in flight.  sched_barrier fences keep the scheduler
+    // from pulling each read down next to its MFMA, which would expose the
+    // whole LDS latency on every MFMA.
+    auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, u32x4 (&kr)[4],
+                     f32x16 (&sc)[2], f32x16 (&sn)[2], float m_use, const uint32_t (&kw)[2][4]) {
       constexpr int NS = 2 * KC;    // S MFMAs per tile
       constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
-      u32x4 kr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[i] = lds_nat(kn + (i / KC) * 32 * (D * 2), nbv, i % KC);
+      constexpr int NP = 4 * DB;    // P V MFMAs per tile
       sn[0] = f32x16{};
       sn[1] = f32x16{};
       float lsum = 0.0f;
       u32x4 pb[4];
+      u32x4 vr[3];
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int kb = i / KC, c = i % KC;
         sn[kb] = mfma32<DT>(kr[i & 3], qreg[c], sn[kb]);
-        if (i + 4 < NS) kr[i & 3] = lds_nat(kn + ((i + 4) / KC) * 32 * (D * 2), nbv, (i + 4) % KC);
+        if (i + 4 < NS) {
+          kr[i & 3] = lds_nat(kn + ((i + 4) / KC) * 32 * (D * 2), nbv, (i + 4) % KC);
+        } else if (i + 4 - NS < 3) {
+          const int j = i + 4 - NS;
+          vr[j] = lds_At<D>(vt + (16 * (j / DB)) * (D * 2), tbv, j % DB);
+        }
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
           const int idx = i * EPS + e;
@@ -330,10 +342,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += lsum;
-      constexpr int NP = 4 * DB;  // P V MFMAs per tile
-      u32x4 vr[3];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) vr[i] = lds_At<D>(vt + (16 * (i / DB)) * (D * 2), tbv, i % DB);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int mk = i / DB, d = i % DB;
@@ -353,10 +361,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       if (t + 2 < t_hi) dma_k(t + 2, kdst);
       dma_v(t + 1, vdst);
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
+      u32x4 kr[4];
+      k_ring(kn, nbv, kr);
       uint32_t kw[2][4];
       keepw(t, kw);
       const float m_use = prep(t, sc);
-      fused(kn, vt, nbv, tbv, sc, sn, m_use, kw);
+      fused(kn, vt, nbv, tbv, kr, sc, sn, m_use, kw);
       dma_wait();
       __syncthreads();
     };
