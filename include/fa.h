@@ -308,7 +308,7 @@ size_t fa_kvcache_workspace_size(int B, int Sq_new, int Hq, int D, int num_split
  */
 typedef enum {
   FA_KERNEL_FWD = 0,
-  FA_KERNEL_BWD_PREPROCESS = 1,
+  FA_KERNEL_BWD_PREPROCESS = 1, /* kept for numbering; no longer launched (the dQ kernel forms the row terms) */
   FA_KERNEL_BWD_DKDV = 2,
   FA_KERNEL_BWD_DQ = 3,
   FA_KERNEL_DECODE_SPLIT = 4,
