@@ -12,12 +12,14 @@
 // kernel runs one wave per SIMD and spends its registers and LDS on bytes in
 // flight.  Its 4 waves take 32-key tiles round robin, each wave streaming
 // its own tiles with no work-group barrier:
-//   * K rows go HBM -> VGPR straight into the A operand of S^T = K Q^T (one
-//     key row per lane, natural order); V rows go HBM -> LDS by DMA into a
-//     wave-private tile and are read back transposed as the A operand of
-//     O^T += V^T P^T;
-//   * four stages: while a tile is computed, the next three tiles' loads
-//     are in flight (48 KB per wave);
+//   * K and V rows go HBM -> LDS by DMA into wave-private tiles, whole
+//     256-byte row pieces per lane group; K is read back in natural order as
+//     the A operand of S^T = K Q^T, V transposed as the A operand of
+//     O^T += V^T P^T.  (Loading K straight into VGPRs in operand order
+//     fetches 32 bytes of each row per instruction, which streams from HBM
+//     about a quarter slower than whole row pieces.)
+//   * two stages: while a tile is computed, the next tile's K and V are in
+//     flight (16 KB per wave; the LDS holds 2 stages x 4 waves x K and V);
 //   * all query heads of the group (Hq / Hkv <= 32) are the 32 columns of the
 //     B operand, so every K/V byte is read once for the whole group;
 //   * the rotated query is split into a 16-bit high part and a 16-bit
@@ -100,15 +102,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   constexpr int BK = 32;  // keys per wave tile
   constexpr int KC = D / 16, DB = D / 32;
   constexpr int VT = BK * D * 2;  // bytes of one wave's V tile
-  // vector-memory instructions per tile load (K fragments past DG are not loaded)
-  constexpr int NKL = DG == D ? KC : (DG + 15) / 16;
-  constexpr int NVM = NKL + VT / 1024;
-  // V tiles, one per wave and stage; four distinct arrays (one per stage) so
-  // a read of one stage is never ordered behind the DMA into another.
+  // vector-memory instructions per tile load: the K and the V copy
+  constexpr int NVM = 2 * (VT / 1024 > 0 ? VT / 1024 : 1);
+  // K and V tiles, one per wave and stage; four distinct arrays (K and V of
+  // each stage) so a read of one is never ordered behind the DMA into another.
+  __shared__ __attribute__((aligned(1024))) char ks0[4 * VT];
+  __shared__ __attribute__((aligned(1024))) char ks1[4 * VT];
   __shared__ __attribute__((aligned(1024))) char vs0[4 * VT];
   __shared__ __attribute__((aligned(1024))) char vs1[4 * VT];
-  __shared__ __attribute__((aligned(1024))) char vs2[4 * VT];
-  __shared__ __attribute__((aligned(1024))) char vs3[4 * VT];
   __shared__ float mbuf[4 * 32], lbuf[4 * 32];
   __shared__ __attribute__((aligned(16))) char apbuf[4 * D];  // rotated k_new row, v_new row
   __shared__ __attribute__((aligned(16))) char qst[33 * D * 2];  // query rows (G * T <= 32), k_new row
@@ -184,10 +185,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
         lds_write128(qst, (32 * D + ch * 8) * 2, v);
       }
     }
+    zero_pad<D, 4 * BK, DG>(ks0, tid, 256);
+    zero_pad<D, 4 * BK, DG>(ks1, tid, 256);
     zero_pad<D, 4 * BK, DG>(vs0, tid, 256);
     zero_pad<D, 4 * BK, DG>(vs1, tid, 256);
-    zero_pad<D, 4 * BK, DG>(vs2, tid, 256);
-    zero_pad<D, 4 * BK, DG>(vs3, tid, 256);
     __syncthreads();
   }
   // Chunk ch (8 elements) of a staged row, rotated at position pos: the
@@ -267,37 +268,34 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   const int t_first = t_lo + w;
   const int n_my = (k_lo < k_hi && t_first < t_hi) ? (t_hi - t_first + 3) / 4 : 0;
 
-  // K rows go straight into VGPRs in A-operand (natural) order; V rows go by
-  // DMA into this wave's LDS tile for the transposed reads.
-  auto load = [&](int t, u32x4 (&ka)[KC], char* vdst) {
+  // K and V rows of tile t go by DMA into this wave's LDS tiles.
+  auto load = [&](int t, char* kdst, char* vdst) {
     const int64_t base = tile_base(t * BK);
-    const uint16_t* krow = p.k_cache + base + (int64_t)r * kvstride;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      // padded head dim: the fragments past DG are zero (and not loaded, so
-      // the vector-memory count per tile is NKL + V blocks)
-      if (DG == D || c < NKL) ka[c] = (DG == D || (2 * c + hf) * 8 < DG) ? gload128(krow + (2 * c + hf) * 8)
-                                                                          : u32x4{0, 0, 0, 0};
-      else ka[c] = u32x4{0, 0, 0, 0};
-    }
+    dma_tile<D, BK, 1, true, DG>(kdst, p.k_cache + base, kvstride, 0, BK, 0, lane);
     dma_tile<D, BK, 1, true, DG>(vdst, p.v_cache + base, kvstride, 0, BK, 0, lane);
   };
+  const uint32_t nb = nat_base<D>(lane);
 
-  // One tile: `ka` / `vt` hold K and V of tile t.
-  auto compute = [&](int t, u32x4 (&ka)[KC], char* vt) {
+  // One tile: `kt` / `vt` hold K and V of tile t.
+  auto compute = [&](int t, char* kt, char* vt) {
     const int j0 = t * BK;
     if (fused && L >= j0 && L < j0 + BK) {
       // This tile holds the appended position: its row takes the rotated
       // k_new and v_new parked in LDS by the prologue instead of the stale
-      // cache row that was streamed in.
+      // cache row that was streamed in (the lanes of that row write it and
+      // are the ones that read its K fragments; LDS accesses of a wave are
+      // ordered, so the transposed V reads see it too).
       if (r == L - j0) {
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          ka[c] = lds_read128(apbuf, (2 * c + hf) * 16);
+          lds_write128(kt, tile_off<D>(r, 2 * c + hf), lds_read128(apbuf, (2 * c + hf) * 16));
           lds_write128(vt, tile_off<D>(r, 2 * c + hf), lds_read128(apbuf + 2 * D, (2 * c + hf) * 16));
         }
       }
     }
+    u32x4 ka[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) ka[c] = lds_nat(kt, nb, c);
     // two independent accumulation chains (high and low query part): one
     // wave per SIMD has no other wave to hide a single chain's MFMA latency
     f32x16 s = f32x16{}, sl = f32x16{};
@@ -386,33 +384,27 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
   // (the stores above retire before the stream's first wait; they are older
   // than every tile load)
 
-  // Four-stage stream: while tile i is computed, tiles i+1 .. i+3 are in
-  // flight.  VMEM operations retire in order, so waiting until only the
-  // later tiles' NVM operations each are outstanding completes tile i.
-  char* v0 = vs0 + w * VT;
-  char* v1 = vs1 + w * VT;
-  char* v2 = vs2 + w * VT;
-  char* v3 = vs3 + w * VT;
-  u32x4 k0[KC], k1[KC], k2[KC], k3[KC];
-  auto stage = [&](int i, u32x4 (&kc)[KC], char* vc, u32x4 (&kn)[KC], char* vn) {
+  // Two-stage stream: while tile i is computed, tile i+1 is in flight.
+  // VMEM operations retire in order, so waiting until only the next tile's
+  // NVM operations are outstanding completes tile i.  The copy into a stage
+  // is issued after the previous use of that stage has been computed (its
+  // LDS reads have returned: the MFMAs consumed them).
+  char* kt0 = ks0 + w * VT;
+  char* kt1 = ks1 + w * VT;
+  char* vt0 = vs0 + w * VT;
+  char* vt1 = vs1 + w * VT;
+  auto stage = [&](int i, char* kc, char* vc, char* kn, char* vn) {
     const int t = t_first + 4 * i;
-    if (i + 3 < n_my) load(t + 12, kn, vn);
+    if (i + 1 < n_my) load(t + 4, kn, vn);
     asm volatile("" ::: "memory");
-    const int later = min(3, n_my - 1 - i);
-    if (later == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NVM));
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NVM));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NVM));
+    if (i + 1 < n_my) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NVM));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     compute(t, kc, vc);
   };
-  if (n_my > 0) load(t_first, k0, v0);
-  if (n_my > 1) load(t_first + 4, k1, v1);
-  if (n_my > 2) load(t_first + 8, k2, v2);
-  for (int i = 0; i < n_my; i += 4) {
-    stage(i, k0, v0, k3, v3);
-    if (i + 1 < n_my) stage(i + 1, k1, v1, k0, v0);
-    if (i + 2 < n_my) stage(i + 2, k2, v2, k1, v1);
-    if (i + 3 < n_my) stage(i + 3, k3, v3, k2, v2);
+  if (n_my > 0) load(t_first, kt0, vt0);
+  for (int i = 0; i < n_my; i += 2) {
+    stage(i, kt0, vt0, kt1, vt1);
+    if (i + 1 < n_my) stage(i + 1, kt1, vt1, kt0, vt0);
   }
 
   // ---- merge the 4 waves: M = max m_w, each wave scaled by 2^(m_w - M) ----
