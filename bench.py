@@ -239,7 +239,7 @@ def run_fwdbwd(args, torch, fa):
     pairs_step = sum(visible_pairs(t["B"], H, t["S"], c) for t in cases for c in (False, True))
     value = flops_step * args.steps / wall / 1e12
     # algorithmic flops per kernel kind: fwd 4D, dK/dV 8D (S, dP, dV, dK), dQ 2D per pair
-    per_pair = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 2 * D, "bwd_preprocess": 0}
+    per_pair = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 2 * D}
     kern = {}
     for name, (ms, n) in prof.items():
         if n == 0:
@@ -387,7 +387,7 @@ def run_copy_calibration(torch):
     print(json.dumps({"copy_bytes": n}))
 
 
-KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"), ("bwd_pre_kernel", "bwd_preprocess"),
+KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
                ("fwd_kernel", "fwd"), ("decode_split_kernel", "decode_split"),
                ("decode_combine_kernel", "decode_combine"))
 
