@@ -302,10 +302,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     // The pipelined block in an explicit instruction order.  S of the next
     // tile: a ring of four K fragments keeps four LDS reads in flight ahead of
     // the MFMA that consumes them, and each MFMA is followed by a slice of the
-    // current tile's softmax (exponentials, row sum, packing of P); once the
-    // K ring has nothing left to fetch, its last slots start the first three
-    // V^T fragments.  Then O += P V with a ring of three V^T fragments (six
-    // transposed reads) in flight.  sched_barrier fences keep the scheduler
+    // current tile's exponentials; once the K ring has nothing left to fetch,
+    // its last slots start the first three V^T fragments.  Then O += P V with
+    // a ring of three V^T fragments (six transposed reads) in flight, with
+    // the packing of P and the row sum spread over those MFMAs, so the
+    // element-wise work is split between both halves of the step.  (Dropout
+    // tiles run the plain loop, never this block.)  sched_barrier fences keep the scheduler
     // from pulling each read down next to its MFMA, which would expose the
     // whole LDS latency on every MFMA.
     auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, u32x4 (&kr)[4],
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       constexpr int NS = 2 * KC;    // S MFMAs per tile
       constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
       constexpr int NP = 4 * DB;    // P V MFMAs per tile
+      constexpr int LEAD = DB >= 2 ? 2 : 1;
       sn[0] = f32x16{};
       sn[1] = f32x16{};
       float lsum = 0.0f;
@@ -331,24 +334,27 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
           const int idx = i * EPS + e;
-          const float pv = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
-          lsum += pv;
-          sc[idx >> 4][idx & 15] = (DROP && !drop_keep(kw[idx >> 4], idx & 15, p.drop.t)) ? 0.0f : pv;
+          sc[idx >> 4][idx & 15] = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
         }
-        if (((i + 1) * EPS) % 8 == 0) {
-          const int mk = (i + 1) * EPS / 8 - 1;
-          pb[mk] = pack_frag_half<DT>(sc[mk >> 1], mk & 1);
-        }
+        // the first P operand is packed here; the other three, and the row
+        // sum, under the P V MFMAs, which carry no other element-wise work
+        if ((i + 1) * EPS == 8) pb[0] = pack_frag_half<DT>(sc[0], 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += lsum;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int mk = i / DB, d = i % DB;
         oacc[d] = mfma32<DT>(vr[i % 3], pb[mk], oacc[d]);
         if (i + 3 < NP) vr[i % 3] = lds_At<D>(vt + (16 * ((i + 3) / DB)) * (D * 2), tbv, (i + 3) % DB);
+        // P operand mn (used from MFMA mn * DB on) is packed LEAD MFMAs ahead
+#pragma unroll
+        for (int mn = 1; mn < 4; ++mn)
+          if (i == mn * DB - LEAD) pb[mn] = pack_frag_half<DT>(sc[mn >> 1], mn & 1);
+#pragma unroll
+        for (int e = i * 32 / NP; e < (i + 1) * 32 / NP; ++e) lsum += sc[e >> 4][e & 15];
         __builtin_amdgcn_sched_barrier(0);
       }
+      l_run += lsum;
     };
 
     // Pipelined step for tile t (t + 1 < t_hi): `sc` holds S of tile t, the
