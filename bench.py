@@ -464,7 +464,7 @@ def main():
         pmc_summary(*args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs one process on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     if args.copy_calibration:

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* a size, pointer, option or alignment is invalid */
-  FA_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for (e.g. D = 80) */
+  FA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for (e.g. D = 80) */
   FA_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than the size query */
   FA_ERR_LAUNCH = 4       /* hipGetLastError reported an error after a launch */
 } fa_status;
