@@ -96,7 +96,7 @@ def _softmax_rows(z, ok):
     """Row softmax over allowed entries: returns (P, LSE); empty rows give
     P = 0 and LSE = +inf."""
     zm = np.where(ok, z, -np.inf)
-    m = zm.max(axis=1)
+    m = zm.max(axis=1, initial=-np.inf)  # no keys at all (Sk = 0) is an empty row too
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
     e = np.where(ok, np.exp(zm - m_safe[:, None]), 0.0)

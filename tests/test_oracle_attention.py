@@ -164,6 +164,14 @@ def test_constant_values_and_empty_rows():
     out, lse = attention_fwd(c.q, c.k, c.v, c.scale, causal=True)
     assert (out[0, :2] == 0).all() and np.isposinf(lse[0, 0, :2]).all()
     assert np.isfinite(lse[0, 0, 2:]).all()
+    # no keys at all (Sk = 0): every row is empty, and so are the gradients
+    c = dense_case(2, 3, 1, 2, 1, 8, "bf16", seed=10)
+    k0, v0 = c.k[:, :0], c.v[:, :0]
+    for causal in (False, True):
+        out, lse = attention_fwd(c.q, k0, v0, c.scale, causal=causal)
+        assert out.shape == (2, 3, 2, 8) and (out == 0).all() and np.isposinf(lse).all()
+        dq, dk, dv = attention_bwd(c.q, k0, v0, c.dout, c.scale, causal=causal)
+        assert (dq == 0).all() and dk.shape == (2, 0, 1, 8) and dv.shape == (2, 0, 1, 8)
 
 
 # ---------------------------------------------------------- invariants ----
