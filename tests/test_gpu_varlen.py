@@ -58,6 +58,27 @@ def test_varlen_unequal_q_k_lengths():
     assert_grad(dv, gv, "dv")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_queries_without_keys_and_keys_without_queries(causal):
+    # sequence 0: queries, no keys (O = 0, LSE = +inf, dQ = 0); sequence 1:
+    # keys, no queries (dK = dV = 0); the rest ordinary.  The dQ kernel writes
+    # the row terms the dK/dV kernel reads, so both kinds of empty side meet.
+    lq, lk = [4, 0, 100, 33], [0, 50, 100, 70]
+    c = varlen_case(lq, lk, Hq=4, Hkv=2, D=128, seed=43, causal=causal)
+    say("varlen empty sides", lq, lk, causal)
+    out, lse, (dq, dk, dv) = _run(c)
+    args = (c.cu_seqlens_q, c.cu_seqlens_k, c.scale, causal)
+    ro, rl = varlen_fwd(c.q, c.k, c.v, *args)
+    assert_out(out, ro, torch.bfloat16)
+    assert_lse(lse, rl)
+    assert torch.isinf(lse[:, :4]).all() and (out[:4] == 0).all()
+    gq, gk, gv = varlen_bwd(c.q, c.k, c.v, c.dout, *args)
+    assert_grad(dq, gq, "dq")
+    assert_grad(dk, gk, "dk")
+    assert_grad(dv, gv, "dv")
+    assert (dq[:4] == 0).all() and (dk[:50] == 0).all() and (dv[:50] == 0).all()
+
+
 def test_cfg4_full_size_sampled():
     c = cfg4()
     say("varlen", c.name)
