@@ -21,7 +21,10 @@ Printed as one JSON line, with
                  1 / 4 / 16 / automatic splits) in HBM GB/s, each timed call
                  preceded by an untimed 1 GiB scratch write so the caches
                  are cold (the warm, back-to-back rate is reported beside
-                 it).
+                 it);
+  memory_vs_naive — extra device memory of one fa_fwd + fa_bwd against
+                 naive attention (scores and softmax materialised, float32
+                 autograd) at S = 2K and 4K of the sweep shape, for context.
 
 Modes: ``--copy-calibration`` runs a plain device copy of known size (for
 scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters); ``--decode-only`` and
@@ -259,6 +262,46 @@ def run_fwdbwd(args, torch, fa):
 
 
 # ---------------------------------------------------------------------------
+def run_memory(torch, fa):
+    """Extra device memory of one fa_fwd + fa_bwd against naive attention
+    (scores, softmax and their gradients materialised by autograd) at
+    S = 2K and 4K of the sweep shape: context for the pages' memory-saving
+    figures, not a target.  The naive side runs in float32 (batched bf16
+    products with transposed operands are kept out of this run)."""
+    from workloads import cfg2
+    dev = torch.device("cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    res = []
+    for S in (2048, 4096):
+        c = cfg2(S, H, D, False)
+        q, k, v, do = (x.to(dev) for x in (c.q, c.k, c.v, c.dout))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out, lse = fa.fa_fwd(q, k, v, scale=scale)
+        grads = fa.fa_bwd(q, k, v, out, do, lse, scale=scale)
+        torch.cuda.synchronize()
+        fused = torch.cuda.max_memory_allocated() - base
+        del out, lse, grads
+        qf, kf, vf = (x.float().permute(0, 2, 1, 3).contiguous().requires_grad_() for x in (q, k, v))
+        dof = do.float().permute(0, 2, 1, 3).contiguous()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        s = torch.matmul(qf, kf.transpose(-1, -2).contiguous()) * scale
+        o = torch.matmul(torch.softmax(s, dim=-1), vf)
+        o.backward(dof)
+        torch.cuda.synchronize()
+        naive = torch.cuda.max_memory_allocated() - base
+        del qf, kf, vf, dof, s, o
+        res.append({"S": S, "B": TOKENS // S, "fused_MiB": round(fused / 2 ** 20, 1),
+                    "naive_fp32_MiB": round(naive / 2 ** 20, 1), "ratio": round(naive / max(fused, 1), 1)})
+        log(f"memory S={S}: {res[-1]}")
+    return res
+
+
 def decode_bytes(L, B, Hq, Hkv, D_, page):
     """Algorithmic HBM bytes of one decode call: K and V rows of every live
     position (+ the appended one), q in, out, k_new/v_new in, appended slots
@@ -477,6 +520,7 @@ def main():
         return
     fb = run_fwdbwd(args, torch, fa)
     dec = None if args.fwdbwd_only else run_decode(args, torch, fa)
+    mem = None if (args.no_extras or args.fwdbwd_only) else run_memory(torch, fa)
     cpu = None if (args.no_cpu_baseline or args.fwdbwd_only) else run_cpu_baseline()
     line = {
         "metric": METRIC,
@@ -503,6 +547,7 @@ def main():
         "head_dims_s4096": fb["by_head_dim"],
         "fwd_bf16_vs_fp8": fb["fp8"],
         "decode": dec,
+        "memory_vs_naive": mem,
     }
     print(json.dumps(line))
 
