@@ -31,17 +31,35 @@ import numpy as np
 from .attention import attention_fwd, _f64
 
 
-def round_bf16(x):
-    """Round float64 values once to the nearest bfloat16 (ties to even);
-    returns float64.  A bfloat16 keeps 8 significant bits."""
+def _round_binary(x, p, emin, emax):
+    """Round float64 values once to the nearest value of a binary floating
+    format with ``p`` significant bits, smallest normal 2^emin and largest
+    exponent emax (ties to even, subnormals below 2^emin, overflow to inf);
+    returns float64.  Division and multiplication by the power-of-two
+    quantum are exact, and ``np.rint`` rounds half to even."""
     x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
-    m = np.rint(m * 256.0) / 256.0          # 8 significant bits, half-to-even
-    return np.ldexp(m, e)
+    ax = np.abs(x)
+    _, e = np.frexp(ax)                     # ax = m * 2^e, 0.5 <= m < 1
+    lead = np.maximum(e - 1, emin)          # exponent of the leading bit (subnormals: emin)
+    quantum = np.ldexp(1.0, lead - (p - 1))
+    with np.errstate(invalid="ignore"):
+        y = np.rint(ax / quantum) * quantum
+    top = np.ldexp(2.0 - np.ldexp(1.0, 1 - p), emax)  # largest finite value
+    y = np.where(y > top, np.inf, y)
+    y = np.where(np.isinf(ax), np.inf, y)
+    return np.copysign(y, x)
+
+
+def round_bf16(x):
+    """Round float64 values once to the nearest bfloat16 (8 significant bits,
+    the exponent range of float32), ties to even; returns float64."""
+    return _round_binary(x, 8, -126, 127)
 
 
 def round_fp16(x):
-    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+    """Round float64 values once to the nearest IEEE binary16 (11 significant
+    bits, smallest normal 2^-14, largest 65504), ties to even; returns float64."""
+    return _round_binary(x, 11, -14, 15)
 
 
 def rotary_apply(x, cos_row, sin_row, rotary_dim):

@@ -7,6 +7,7 @@ import torch
 
 from oracle import (attention_fwd, attention_bwd, varlen_fwd, varlen_bwd, rotary_apply,
                     round_bf16, kvcache_fwd, gather_logical_cache)
+from oracle.kvcache import round_fp16
 from workloads import (varlen_case, varlen_lengths, decode_case, rotary_tables, dense_case,
                        cfg4, cfg5)
 
@@ -103,6 +104,57 @@ def test_round_bf16_matches_torch():
     ref = torch.from_numpy(x32).to(torch.bfloat16).to(F64).numpy()
     np.testing.assert_array_equal(round_bf16(x32.astype(np.float64)), ref)
     assert round_bf16(1 + 2 ** -8) == 1.0 and round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+
+
+def _all_finite(kind):
+    """Every finite value of a 16-bit format, ascending, as float64 (the
+    65536 bit patterns decoded by numpy / torch, NaNs and infinities dropped)."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    if kind == "fp16":
+        vals = bits.view(np.float16).astype(np.float64)
+    else:
+        vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(F64).numpy()
+    vals = np.unique(vals[np.isfinite(vals)])  # +0 and -0 merge
+    return vals
+
+
+@pytest.mark.parametrize("kind", ["fp16", "bf16"])
+def test_round16_exhaustive_ties_and_neighbours(kind):
+    """Round-to-nearest-even against the format itself: every finite value is
+    kept; every midpoint of two neighbours goes to the one with an even last
+    significand bit; a float64 step either side of the midpoint goes to the
+    nearer neighbour (a rounder that passed through float32 first would send
+    those to the even one); past the largest value by half an ulp is inf."""
+    rnd = round_fp16 if kind == "fp16" else round_bf16
+    vals = _all_finite(kind)
+    np.testing.assert_array_equal(rnd(vals), vals)
+    a, b = vals[:-1], vals[1:]
+    mid = (a + b) / 2.0  # exact: one more bit than the format
+    # the neighbour whose last significand bit is 0
+    bits_a = (np.asarray(a, np.float16).view(np.uint16) if kind == "fp16"
+              else torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16))
+    even = np.where((bits_a & 1) == 0, a, b)
+    np.testing.assert_array_equal(rnd(mid), even)
+    np.testing.assert_array_equal(rnd(np.nextafter(mid, -np.inf)), a)
+    np.testing.assert_array_equal(rnd(np.nextafter(mid, np.inf)), b)
+    top = vals[-1]
+    half_ulp = (top - vals[-2]) / 2.0
+    assert rnd(top + half_ulp) == np.inf and rnd(np.nextafter(top + half_ulp, 0.0)) == top
+    assert rnd(-(top + half_ulp)) == -np.inf
+    assert np.isnan(rnd(np.nan)) and rnd(np.inf) == np.inf
+
+
+def test_round_fp16_matches_torch():
+    """float32 inputs (one rounding in torch's float32 -> float16 cast), over
+    the normal and subnormal range of binary16, with exact float32 ties."""
+    rng = np.random.default_rng(5)
+    x32 = (rng.standard_normal(40000) * np.exp2(rng.uniform(-27, 17, 40000))).astype(np.float32)
+    ties = np.float32([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -25, 3 * 2 ** -25, -(1 + 2 ** -11), 65520.0, 65519.0])
+    x32 = np.concatenate([x32, ties])
+    ref = torch.from_numpy(x32).to(torch.float16).to(F64).numpy()
+    np.testing.assert_array_equal(round_fp16(x32.astype(np.float64)), ref)
+    assert round_fp16(1 + 2 ** -11) == 1.0 and round_fp16(1 + 3 * 2 ** -11) == 1 + 2 ** -9
+    assert round_fp16(2 ** -25) == 0.0 and round_fp16(3 * 2 ** -25) == 2 ** -23
 
 
 # ------------------------------------------------------------ kvcache ----
