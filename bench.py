@@ -98,29 +98,66 @@ def recorded_traffic(kernel):
 
 
 # ---------------------------------------------------------------------------
-def run_fwdbwd(args, torch, fa):
+def time_ms(torch, fn, reps=3, warm=1):
+    """Mean time of `fn` over `reps` calls, from HIP events on the current
+    stream, after `warm` untimed calls."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep_cases(torch, fa, H_, D_):
+    """Device inputs of the hidden-2048 sweep at (H_, D_): one dict per S."""
     from workloads import cfg2
     dev = torch.device("cuda:0")
     cases = []
     for S in SEQLENS:
-        c = cfg2(S, H, D, False)
+        c = cfg2(S, H_, D_, False)
         B = TOKENS // S
-        t = dict(S=S, B=B, q=c.q.to(dev), k=c.k.to(dev), v=c.v.to(dev), do=c.dout.to(dev))
+        t = dict(S=S, B=B, H=H_, D=D_, q=c.q.to(dev), k=c.k.to(dev), v=c.v.to(dev), do=c.dout.to(dev))
         t["out"] = torch.empty_like(t["q"])
-        t["lse"] = torch.empty(B, H, S, device=dev, dtype=torch.float32)
+        t["lse"] = torch.empty(B, H_, S, device=dev, dtype=torch.float32)
         t["dq"] = torch.empty_like(t["q"])
         t["dk"] = torch.empty_like(t["k"])
         t["dv"] = torch.empty_like(t["v"])
-        ws = fa.lib().fa_bwd_workspace_size(B, S, S, H, H, D, 0)
+        ws = fa.lib().fa_bwd_workspace_size(B, S, S, H_, H_, D_, 0)
         t["ws"] = torch.empty(ws, device=dev, dtype=torch.uint8)
         cases.append(t)
-        log(f"inputs ready S={S}")
+        log(f"inputs ready H={H_} D={D_} S={S}")
+    return cases
+
+
+def fwdbwd_once(fa, t, causal):
+    scale = 1.0 / math.sqrt(t["D"])
+    fa.fa_fwd(t["q"], t["k"], t["v"], out=t["out"], lse=t["lse"], scale=scale, causal=causal)
+    fa.fa_bwd(t["q"], t["k"], t["v"], t["out"], t["do"], t["lse"], dq=t["dq"], dk=t["dk"], dv=t["dv"],
+              scale=scale, causal=causal, workspace=t["ws"])
+
+
+def per_config(torch, fa, cases, reps=3):
+    per = []
+    for t in cases:
+        for causal in (False, True):
+            ms = time_ms(torch, lambda: fwdbwd_once(fa, t, causal), reps=reps, warm=0)
+            fl = 14 * t["D"] * visible_pairs(t["B"], t["H"], t["S"], causal)
+            per.append({"S": t["S"], "B": t["B"], "H": t["H"], "D": t["D"], "causal": causal,
+                        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
+    return per
+
+
+def run_fwdbwd(args, torch, fa):
+    dev = torch.device("cuda:0")
+    cases = sweep_cases(torch, fa, H, D)
     scale = 1.0 / math.sqrt(D)
 
     def one(t, causal):
-        fa.fa_fwd(t["q"], t["k"], t["v"], out=t["out"], lse=t["lse"], scale=scale, causal=causal)
-        fa.fa_bwd(t["q"], t["k"], t["v"], t["out"], t["do"], t["lse"], dq=t["dq"], dk=t["dk"], dv=t["dv"],
-                  scale=scale, causal=causal, workspace=t["ws"])
+        fwdbwd_once(fa, t, causal)
 
     def step():
         for t in cases:
@@ -131,20 +168,7 @@ def run_fwdbwd(args, torch, fa):
         step()
     torch.cuda.synchronize()
     # per-config timing (separate, untimed for the headline)
-    per = []
-    for t in cases:
-        for causal in (False, True):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 3
-            e0.record()
-            for _ in range(reps):
-                one(t, causal)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
-            per.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
-                        "tflops": round(fl / ms / 1e9, 1)})
+    per = per_config(torch, fa, cases)
     # dropout (p = 0.1) on the long sequences, reported beside the headline
     drop = []
     for t in ([] if args.no_extras else cases):
@@ -256,9 +280,94 @@ def run_fwdbwd(args, torch, fa):
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic(dom),
-                "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"]}
+                "avg_launch_ms": kern[dom]["avg_launch_ms"], "launches": kern[dom]["launches"],
+                "flop_per_launch": per_pair[dom] * pairs_step / (2 * len(cases)),
+                "count": f"{per_pair[dom] // D}*D flop per visible (query, key) pair, averaged over the "
+                         f"{2 * len(cases)} launches of one step"}
     return dict(value=value, ms_per_step=wall / args.steps * 1e3, per_config=per, kernels=kern,
                 roofline=roofline, flops_step=flops_step, dropout=drop, by_head_dim=by_d, fp8=fp8)
+
+
+# ---------------------------------------------------------------------------
+def run_configs(args, torch, fa):
+    """The other workloads of the path, each timed on its own (HIP events,
+    mean of several calls after warm-up calls):
+      cfg1  — forward only, fp16, (2, 512, 16, 64), causal, scale 1/8;
+      hd64  — the hidden-2048 fwd+bwd sweep at H = 32, D = 64;
+      cfg3  — GQA 32/8, S = 8192, D = 128, causal, window (4096, 0), softcap 30, ALiBi;
+      cfg4  — packed varlen, 32768 tokens in 13 sequences (lengths U[128, 4096]),
+              H = 16, D = 128, causal.
+    Work is 4 D (forward) and 14 D (fwd+bwd) flop per visible (query, key)
+    pair, counted exactly from the masks."""
+    from workloads import cfg1, cfg3, cfg4
+    dev = torch.device("cuda:0")
+    res = {}
+    # cfg1: a launch-latency-sized forward; the mean over many calls
+    c = cfg1()
+    q, k, v = (x.to(dev) for x in (c.q, c.k, c.v))
+    out, lse = torch.empty_like(q), torch.empty(2, 16, 512, device=dev)
+    ms = time_ms(torch, lambda: fa.fa_fwd(q, k, v, out=out, lse=lse, scale=c.scale, causal=True), reps=200, warm=20)
+    pairs = 2 * 16 * pairs_causal(512)
+    res["cfg1_fwd_fp16"] = {"workload": c.name, "pairs": pairs, "us_per_call": round(ms * 1e3, 2),
+                            "tflops": round(4 * 64 * pairs / ms / 1e9, 1)}
+    log(f"cfg1: {res['cfg1_fwd_fp16']}")
+    # hd64 sweep
+    cases = sweep_cases(torch, fa, 32, 64)
+    for t in cases:
+        for causal in (False, True):
+            fwdbwd_once(fa, t, causal)
+    torch.cuda.synchronize()
+    res["sweep_hd64"] = per_config(torch, fa, cases, reps=5)
+    del cases
+    log(f"hd64 sweep: {[r['tflops'] for r in res['sweep_hd64']]}")
+    # cfg3
+    c = cfg3()
+    q, k, v, do = (x.to(dev) for x in (c.q, c.k, c.v, c.dout))
+    al = c.alibi_slopes.to(dev)
+    kw = dict(scale=c.scale, causal=True, window=c.window, softcap=c.softcap, alibi_slopes=al)
+    out, lse = torch.empty_like(q), torch.empty(1, 32, 8192, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.lib().fa_bwd_workspace_size(1, 8192, 8192, 32, 8, 128, 0), device=dev, dtype=torch.uint8)
+    S, wl = 8192, c.window[0]
+    pairs = 32 * sum(min(i, wl) + 1 for i in range(S))
+
+    def f3():
+        fa.fa_fwd(q, k, v, out=out, lse=lse, **kw)
+
+    def fb3():
+        f3()
+        fa.fa_bwd(q, k, v, out, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    ms_f, ms_fb = time_ms(torch, f3, reps=10, warm=2), time_ms(torch, fb3, reps=10, warm=2)
+    res["cfg3_gqa_window_softcap_alibi"] = {
+        "workload": c.name, "pairs": pairs, "fwd_ms": round(ms_f, 4), "fwd_tflops": round(4 * 128 * pairs / ms_f / 1e9, 1),
+        "fwdbwd_ms": round(ms_fb, 4), "fwdbwd_tflops": round(14 * 128 * pairs / ms_fb / 1e9, 1)}
+    log(f"cfg3: {res['cfg3_gqa_window_softcap_alibi']}")
+    del q, k, v, do, out, lse, dq, dk, dv, ws
+    # cfg4
+    c = cfg4()
+    q, k, v, do = (x.to(dev) for x in (c.q, c.k, c.v, c.dout))
+    cq, ck = c.cu_seqlens_q.to(dev), c.cu_seqlens_k.to(dev)
+    lens = [int(b - a) for a, b in zip(c.cu_seqlens_q.tolist()[:-1], c.cu_seqlens_q.tolist()[1:])]
+    pairs = 16 * sum(pairs_causal(L) for L in lens)
+    out, lse = torch.empty_like(q), torch.empty(16, q.shape[0], device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.lib().fa_bwd_varlen_workspace_size(q.shape[0], 16, 128, 0), device=dev, dtype=torch.uint8)
+    mq, mk = c.max_seqlen_q, c.max_seqlen_k
+
+    def f4():
+        fa.fa_fwd_varlen(q, k, v, cq, ck, mq, mk, out=out, lse=lse, scale=c.scale, causal=True)
+
+    def fb4():
+        f4()
+        fa.fa_bwd_varlen(q, k, v, out, do, lse, cq, ck, mq, mk, dq=dq, dk=dk, dv=dv, scale=c.scale, causal=True,
+                         workspace=ws)
+    ms_f, ms_fb = time_ms(torch, f4, reps=10, warm=2), time_ms(torch, fb4, reps=10, warm=2)
+    res["cfg4_varlen"] = {
+        "workload": c.name, "seqlens": lens, "pairs": pairs, "fwd_ms": round(ms_f, 4),
+        "fwd_tflops": round(4 * 128 * pairs / ms_f / 1e9, 1), "fwdbwd_ms": round(ms_fb, 4),
+        "fwdbwd_tflops": round(14 * 128 * pairs / ms_fb / 1e9, 1)}
+    log(f"cfg4: {res['cfg4_varlen']}")
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -313,6 +422,10 @@ def decode_bytes(L, B, Hq, Hkv, D_, page):
 
 
 def run_decode(args, torch, fa, splits=16):
+    """Paged decode at num_splits 1, 4, `splits` and automatic (or only
+    --decode-splits N); with --cold-only every call, warm-up included, follows
+    a scratch write, and no back-to-back (warm) calls are made, so a profile
+    of the run holds cold calls only."""
     from workloads import cfg5
     dev = torch.device("cuda:0")
     c = cfg5()
@@ -331,27 +444,33 @@ def run_decode(args, torch, fa, splits=16):
     nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
     res = {}
     # 0 = the library's automatic choice
-    for ns in [1, 4, splits, 0] if splits not in (1, 4, 0) else [1, 4, 0]:
+    split_list = [args.decode_splits] if args.decode_splits is not None else (
+        [1, 4, splits, 0] if splits not in (1, 4, 0) else [1, 4, 0])
+    for ns in split_list:
         ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
                          dtype=torch.uint8)
 
         def call():
             fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
                               scale=c.scale, workspace=ws)
-        for _ in range(5):
+        for i in range(5):
+            if args.cold_only:
+                scratch.fill_(i & 255)
             call()
         torch.cuda.synchronize()
-        fa.profiler_enable(1024)
-        fa.profiler_reset()
         reps = max(10, args.steps * 5)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            call()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / reps
-        prof = fa.profiler_read()
-        fa.profiler_disable()
-        warm_split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
+        wall = warm_split_ms = float("nan")
+        if not args.cold_only:
+            fa.profiler_enable(1024)
+            fa.profiler_reset()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / reps
+            prof = fa.profiler_read()
+            fa.profiler_disable()
+            warm_split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
         # cold: every timed call follows the scratch write
         fa.profiler_enable(1024)
         fa.profiler_reset()
@@ -373,8 +492,10 @@ def run_decode(args, torch, fa, splits=16):
                    "GBps": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
                    "split_kernel_us": round(split_ms * 1e3, 1), "combine_kernel_us": round(comb_ms * 1e3, 1),
                    "split_kernel_GBps": round(nbytes / (split_ms * 1e-3) / 1e9, 1),
-                   "warm_us_per_call": round(wall * 1e6, 1), "warm_GBps": round(nbytes / wall / 1e9, 1),
-                   "warm_split_kernel_GBps": round(nbytes / (warm_split_ms * 1e-3) / 1e9, 1)}
+                   "split_kernel_avg_us_all_launches": round(split_ms * 1e3, 2),
+                   "warm_us_per_call": None if args.cold_only else round(wall * 1e6, 1),
+                   "warm_GBps": None if args.cold_only else round(nbytes / wall / 1e9, 1),
+                   "warm_split_kernel_GBps": None if args.cold_only else round(nbytes / (warm_split_ms * 1e-3) / 1e9, 1)}
         log(f"decode splits={ns}: {res[ns]}")
     best = max(res.values(), key=lambda r: r["GBps"])
     return {"workload": "decode bf16 B=8 Hq=32 Hkv=8 D=128 page=256 rotary128, cache_seqlens seed 5",
@@ -390,32 +511,83 @@ def run_decode(args, torch, fa, splits=16):
 CPU_HEADS = 12  # heads in the oracle's timed sample
 
 
+def host_info():
+    """CPU model, the CPUs this process may run on, and numpy's BLAS."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_threads():
+    """Threads for the oracle's BLAS: the CPUs of this process's affinity
+    mask, capped by OMP_NUM_THREADS when the environment sets it (a shared
+    host's share)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
 def run_cpu_baseline():
     """The float64 oracle on a bounded sample (about 10-20 s of host work):
     the batch-0 slice of the first CPU_HEADS heads of the same inputs for S in
-    {512, 1K, 2K, 4K}, non-causal and causal."""
-    import numpy as np  # noqa: F401
+    {512, 1K, 2K, 4K}, non-causal and causal; BLAS threads set explicitly."""
+    from threadpoolctl import threadpool_limits
     from oracle import attention_fwd, attention_bwd
     from workloads import cfg2
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    n = cpu_threads()
     flops, secs = 0.0, 0.0
-    for S in (512, 1024, 2048, 4096):
-        c = cfg2(S, H, D, False)
-        q, k, v, do = (t[:1, :, :CPU_HEADS] for t in (c.q, c.k, c.v, c.dout))
-        for causal in (False, True):
-            t0 = time.perf_counter()
-            attention_fwd(q, k, v, c.scale, causal)
-            attention_bwd(q, k, v, do, c.scale, causal, check_delta=False)
-            secs += time.perf_counter() - t0
-            flops += CPU_HEADS * 14 * D * (pairs_causal(S) if causal else S * S)
-    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    with threadpool_limits(limits=n):
+        for S in (512, 1024, 2048, 4096):
+            c = cfg2(S, H, D, False)
+            q, k, v, do = (t[:1, :, :CPU_HEADS] for t in (c.q, c.k, c.v, c.dout))
+            for causal in (False, True):
+                t0 = time.perf_counter()
+                attention_fwd(q, k, v, c.scale, causal)
+                attention_bwd(q, k, v, do, c.scale, causal, check_delta=False)
+                secs += time.perf_counter() - t0
+                flops += CPU_HEADS * 14 * D * (pairs_causal(S) if causal else S * S)
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
             "sample": f"float64 numpy oracle, fwd+bwd of the batch-0 slice of heads 0..{CPU_HEADS - 1} of the "
                       "sweep inputs for S in {512,1K,2K,4K}, non-causal and causal; same 14*D*pairs flop count",
-            "seconds": round(secs, 2)}
+            "seconds": round(secs, 2), "host": host_info()}
+
+
+def run_cpu_decode():
+    """The float64 oracle's decode (rotary, gather through the block table,
+    append, attention over every cached key) on the whole paged-decode
+    workload, timed on the host: GB/s with the same byte count as the GPU."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kvcache_fwd
+    from workloads import cfg5
+    c = cfg5()
+    n = cpu_threads()
+    with threadpool_limits(limits=n):
+        t0 = time.perf_counter()
+        kvcache_fwd(c.q, c.k_new, c.v_new, c.k_cache, c.v_cache, c.cache_seqlens, c.block_table, c.page_size,
+                    c.rotary_cos, c.rotary_sin, c.rotary_dim, c.scale)
+        secs = time.perf_counter() - t0
+    nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": "the whole decode call (B=8, Hq=32, Hkv=8, D=128, page 256, cache lengths seed 5), "
+                      "float64 numpy oracle", "seconds": round(secs, 2), "bytes": nbytes}
 
 
 def run_copy_calibration(torch):
@@ -498,6 +670,10 @@ def main():
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--fwdbwd-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-splits", type=int, default=None,
+                    help="time the decode at this num_splits only (0 = automatic)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="decode: only cold calls (each after a scratch write), for profiles")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dropout, head-dim and fp8 side measurements (profiling runs)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -520,8 +696,11 @@ def main():
         return
     fb = run_fwdbwd(args, torch, fa)
     dec = None if args.fwdbwd_only else run_decode(args, torch, fa)
+    cfgs = None if (args.no_extras or args.fwdbwd_only) else run_configs(args, torch, fa)
     mem = None if (args.no_extras or args.fwdbwd_only) else run_memory(torch, fa)
     cpu = None if (args.no_cpu_baseline or args.fwdbwd_only) else run_cpu_baseline()
+    if dec is not None and not args.no_cpu_baseline:
+        dec["cpu_baseline"] = run_cpu_decode()
     line = {
         "metric": METRIC,
         "value": round(fb["value"], 2),
@@ -546,6 +725,7 @@ def main():
         "dropout_p0.1": fb["dropout"],
         "head_dims_s4096": fb["by_head_dim"],
         "fwd_bf16_vs_fp8": fb["fp8"],
+        "configs": cfgs,
         "decode": dec,
         "memory_vs_naive": mem,
     }

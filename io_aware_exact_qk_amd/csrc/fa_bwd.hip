@@ -774,10 +774,19 @@ static int bwd_varlen(const void* q, const void* k, const void* v, const void* o
   if (st) return st;
   if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
   if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return FA_ERR_INVALID_ARG;
-  if (!bwd_ptrs_ok(q, k, v, out, dout, lse, dq, dk, dv, alibi_slopes)) return FA_ERR_INVALID_ARG;
+  // tensors of an empty side (no queries at all, or no keys at all) may be NULL
+  const bool q_ok = total_q == 0 || (aligned16(q) && aligned16(out) && aligned16(dout) && aligned16(dq) &&
+                                     aligned4(lse));
+  const bool k_ok = total_k == 0 || (aligned16(k) && aligned16(v) && aligned16(dk) && aligned16(dv));
+  if (!q_ok || !k_ok || (alibi_slopes && !aligned4(alibi_slopes))) return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_varlen_workspace_size(total_q, Hq, D, deterministic);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
-  if (total_q == 0 || total_k == 0) return FA_OK;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
+  if (total_q == 0 && total_k == 0) return FA_OK;
+  // With keys but no queries the dK/dV kernel still runs and writes dK = dV = 0
+  // for every key row of a sequence; with queries but no keys the dQ kernel
+  // writes dQ = 0.  Neither reads the tensors of the empty side.
+  if (total_q == 0) max_seqlen_q = 0;
+  if (total_k == 0) max_seqlen_k = 0;
   BwdParams p{};
   fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
               alibi_slopes);

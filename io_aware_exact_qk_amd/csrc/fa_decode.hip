@@ -293,6 +293,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecParams p) {
         }
       }
     }
+    if (j0 + BK > n_keys && r >= n_keys - j0) {
+      // Rows past the last key hold whatever the page holds there (never
+      // written, recycled, or the pre-append slot of a later call); their
+      // weights are 0, but 0 * inf or 0 * NaN in P V would not be, so their
+      // V rows are zeroed (their logits are masked below).
+#pragma unroll
+      for (int c = 0; c < KC; ++c) lds_write128(vt, tile_off<D>(r, 2 * c + hf), u32x4{0, 0, 0, 0});
+    }
     u32x4 ka[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) ka[c] = lds_nat(kt, nb, c);

@@ -610,7 +610,9 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
   if (st) return st;
   if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
   if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FA_ERR_INVALID_ARG;
+  // tensors of an empty side (no queries at all, or no keys at all) may be NULL
+  if (total_q > 0 && (!aligned16(q) || !aligned16(out))) return FA_ERR_INVALID_ARG;
+  if (total_k > 0 && (!aligned16(k) || !aligned16(v))) return FA_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
   if (max_seqlen_q == 0 || total_q == 0) return FA_OK;

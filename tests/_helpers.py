@@ -56,19 +56,64 @@ def assert_grad(got, ref, what, mask=None):
     return e
 
 
-def assert_out_rounded(got, ref, dtype, what="out"):
-    """Output tolerance plus half an ulp of the reference value in the output
-    dtype, per element.
+def visible_dense(Sq, Sk, causal=False, window=(-1, -1)):
+    """Visible keys per query row of a dense call, shaped (1, Sq, 1) to
+    broadcast against an output's (B, Sq, Hq) rows."""
+    from oracle import allowed_mask
+    return allowed_mask(np.arange(Sq), Sq, Sk, causal, window).sum(axis=1)[None, :, None]
 
-    Used where rows with one to a few visible keys (O close to a single v)
-    or dropout's 1/(1-p) scaling put |O| where rounding the result once to
-    16 bits, together with the 16-bit P operand of the PV product, already
-    reaches the plain tolerance: e.g. row 1 of a causal D = 256 bf16 case
-    gives 1.089e-2 both from the kernel and from the standard arithmetic
-    emulated on the CPU (float32 P rounded to bf16, output rounded once)."""
+
+def visible_varlen(cu_q, cu_k, causal=False, window=(-1, -1)):
+    """Visible keys per packed query row of a varlen call, shaped (total_q, 1)."""
+    from oracle import allowed_mask
+    cq = [int(x) for x in (cu_q.tolist() if hasattr(cu_q, "tolist") else cu_q)]
+    ck = [int(x) for x in (cu_k.tolist() if hasattr(cu_k, "tolist") else cu_k)]
+    out = np.zeros((cq[-1], 1), np.int64)
+    for s in range(len(cq) - 1):
+        a, b, n = cq[s], cq[s + 1], ck[s + 1] - ck[s]
+        if b > a:
+            out[a:b, 0] = allowed_mask(np.arange(b - a), b - a, n, causal, window).sum(axis=1)
+    return out
+
+
+FEW_KEYS = 3  # rows with at most this many visible keys get the rounding margin
+
+
+def assert_out_rounded(got, ref, dtype, visible, what="out"):
+    """Output tolerance for shapes with very short rows.
+
+    Every element is held to the plain bound TOL_OUT except two kinds, which
+    get TOL_OUT plus half an ulp of the reference value in the output dtype:
+    rows with at most FEW_KEYS visible keys (O close to a single v, so the
+    16-bit P operand of the PV product and the one rounding of the output
+    already reach the plain bound: e.g. row 1 of a causal D = 256 bf16 case
+    gives 1.089e-2 from the kernel and from that arithmetic emulated on the
+    CPU), and elements with |O_ref| >= 2 (half an ulp there is >= 3.9e-3 in
+    bf16).  ``visible`` holds the visible-key count of each output row and
+    broadcasts against ref.shape[:-1].  Prints how many rows needed the
+    margin."""
     g, r = np64(got), np.asarray(ref, np.float64)
     mant = 7 if dtype == torch.bfloat16 else 10
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - mant)
-    err = np.where(np.isinf(g) & np.isinf(r), 0.0, np.abs(g - r))
-    bad = ~(err <= TOL_OUT[dtype] + 0.5 * ulp)
-    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond tolerance, max err {float(np.nanmax(err)):.3e}"
+    err = np.where(np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r)), 0.0, np.abs(g - r))
+    err = np.where(np.isnan(err), np.inf, err)
+    few = np.broadcast_to(np.asarray(visible) <= FEW_KEYS, r.shape[:-1])[..., None]
+    exempt = few | (np.abs(r) >= 2.0)
+    tol = TOL_OUT[dtype]
+    bound = np.where(exempt, tol + 0.5 * ulp, tol)
+    bad = ~(err <= bound)
+    plain = float(err[~exempt].max()) if (~exempt).any() else 0.0
+    used_rows = int((exempt & (err > tol)).any(axis=-1).sum())
+    say(f"{what}: max err {plain:.3e} on plain-bound elements; {used_rows} rows used the rounding margin")
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond tolerance, max err "
+                           f"{float(err.max()):.3e} (plain-bound max {plain:.3e})")
+
+
+def tile_rows(S, tile, seed):
+    """One seeded row in every `tile`-row block of [0, S), plus rows 0 and
+    S - 1 (sorted, unique): a sample that meets every tile of a launch."""
+    rng = np.random.default_rng(seed)
+    rows = {0, S - 1}
+    for t0 in range(0, S, tile):
+        rows.add(int(t0 + rng.integers(0, min(tile, S - t0))))
+    return sorted(rows)

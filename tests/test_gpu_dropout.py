@@ -14,7 +14,7 @@ import io_aware_exact_qk_amd as fa
 from oracle import attention_fwd, attention_bwd, varlen_fwd, varlen_bwd
 from oracle.dropout import keep_mask, keep_scale
 from workloads import dense_case, varlen_case
-from _helpers import DEV, assert_lse, assert_grad, assert_out_rounded, say
+from _helpers import DEV, assert_lse, assert_grad, assert_out_rounded, say, visible_dense, visible_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_dropout_fwd_bwd(case):
     torch.cuda.synchronize()
     drop = (p, seed, off)
     ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, causal, window, softcap, c.alibi_slopes, dropout=drop)
-    assert_out_rounded(out, ro, c.q.dtype)
+    assert_out_rounded(out, ro, c.q.dtype, visible_dense(Sq, Sk, causal, window))
     assert_lse(lse, rl)
     gq, gk, gv = attention_bwd(c.q, c.k, c.v, c.dout, c.scale, causal, window, softcap, c.alibi_slopes,
                                dropout=drop)
@@ -133,7 +133,7 @@ def test_dropout_varlen():
     torch.cuda.synchronize()
     drop = (p, seed, off)
     ro, rl = varlen_fwd(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, c.scale, True, dropout=drop)
-    assert_out_rounded(out, ro, c.q.dtype)
+    assert_out_rounded(out, ro, c.q.dtype, visible_varlen(c.cu_seqlens_q, c.cu_seqlens_k, True))
     assert_lse(lse, rl)
     gq, gk, gv = varlen_bwd(c.q, c.k, c.v, c.dout, c.cu_seqlens_q, c.cu_seqlens_k, c.scale, True, dropout=drop)
     assert_grad(dq, gq, "dq")

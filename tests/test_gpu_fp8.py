@@ -9,7 +9,7 @@ import torch
 import io_aware_exact_qk_amd as fa
 from oracle import attention_fwd
 from workloads import dense_case
-from _helpers import DEV, assert_out_rounded, assert_lse, say
+from _helpers import DEV, assert_out_rounded, assert_lse, say, visible_dense
 
 pytestmark = pytest.mark.gpu
 F8 = torch.float8_e4m3fn
@@ -58,7 +58,7 @@ def test_fp8_forward(case):
     torch.cuda.synchronize()
     ro, rl = attention_fwd(qd.numpy(), kd.numpy(), vd.numpy(), c.scale, causal, window, softcap,
                            c.alibi_slopes)
-    assert_out_rounded(out, ro, torch.bfloat16)
+    assert_out_rounded(out, ro, torch.bfloat16, visible_dense(Sq, Sk, causal, window))
     assert_lse(lse, rl)
 
 

@@ -1,7 +1,8 @@
 """Head dims 32, 96 and 256 (besides 64 and 128): forward and backward parity
 with the oracle over the option mixes, varlen, dropout and the packed entry
 points, at sizes that span several tiles with ragged tails.  Outputs use the
-rounding-aware bound of _helpers.assert_out_rounded (short causal rows)."""
+plain bound except on rows with at most three visible keys and on
+|O| >= 2 (_helpers.assert_out_rounded)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import torch
 import io_aware_exact_qk_amd as fa
 from oracle import attention_fwd, attention_bwd, varlen_fwd, varlen_bwd
 from workloads import dense_case, varlen_case
-from _helpers import DEV, assert_out_rounded, assert_lse, assert_grad, say
+from _helpers import DEV, assert_out_rounded, assert_lse, assert_grad, say, visible_dense, visible_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +43,7 @@ def test_fwd_bwd(case):
     dq, dk, dv = fa.fa_bwd(q, k, v, out, do, lse, **_kw(c))
     torch.cuda.synchronize()
     ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, causal, window, softcap, c.alibi_slopes)
-    assert_out_rounded(out, ro, c.q.dtype)
+    assert_out_rounded(out, ro, c.q.dtype, visible_dense(Sq, Sk, causal, window))
     assert_lse(lse, rl)
     gq, gk, gv = attention_bwd(c.q, c.k, c.v, c.dout, c.scale, causal, window, softcap, c.alibi_slopes)
     if Sk == 1:
@@ -68,7 +69,7 @@ def test_varlen(D):
                                   scale=c.scale, causal=True)
     torch.cuda.synchronize()
     ro, rl = varlen_fwd(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, c.scale, True)
-    assert_out_rounded(out, ro, c.q.dtype)
+    assert_out_rounded(out, ro, c.q.dtype, visible_varlen(c.cu_seqlens_q, c.cu_seqlens_k, True))
     assert_lse(lse, rl)
     gq, gk, gv = varlen_bwd(c.q, c.k, c.v, c.dout, c.cu_seqlens_q, c.cu_seqlens_k, c.scale, True)
     assert_grad(dq, gq, "dq")
@@ -90,7 +91,7 @@ def test_dropout_and_packed(D):
     torch.cuda.synchronize()
     assert torch.equal(out_p, out_u) and torch.equal(lse_p, lse_u)
     ro, rl = attention_fwd(c.q, c.k, c.v, c.scale, True, dropout=drop)
-    assert_out_rounded(out, ro, c.q.dtype)
+    assert_out_rounded(out, ro, c.q.dtype, visible_dense(160, 160, True))
     assert_lse(lse, rl)
     gq, gk, gv = attention_bwd(c.q, c.k, c.v, c.dout, c.scale, True, dropout=drop)
     assert_grad(dq, gq, "dq")

@@ -6,7 +6,7 @@ import torch
 import io_aware_exact_qk_amd as fa
 from oracle import varlen_fwd, varlen_bwd, attention_fwd, attention_bwd
 from workloads import varlen_case, cfg4
-from _helpers import DEV, assert_out, assert_lse, assert_grad, say
+from _helpers import DEV, assert_out, assert_lse, assert_grad, say, np64, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -79,32 +79,58 @@ def test_varlen_queries_without_keys_and_keys_without_queries(causal):
     assert (dq[:4] == 0).all() and (dk[:50] == 0).all() and (dv[:50] == 0).all()
 
 
+@pytest.mark.parametrize("side", ["no_keys", "no_queries"])
+def test_varlen_one_side_empty_everywhere(side):
+    """total_k = 0: O = 0, LSE = +inf and dQ = 0 are written (over NaN-filled
+    buffers); total_q = 0: dK = dV = 0 are written.  The empty side's tensors
+    have no storage at all."""
+    lq, lk = ([5, 130, 1], [0, 0, 0]) if side == "no_keys" else ([0, 0, 0], [7, 140, 2])
+    c = varlen_case(lq, lk, Hq=4, Hkv=2, D=128, seed=44, causal=False)
+    q, k, v, do = (t.to(DEV) for t in (c.q, c.k, c.v, c.dout))
+    cq, ck = c.cu_seqlens_q.to(DEV), c.cu_seqlens_k.to(DEV)
+    nan = float("nan")
+    out = torch.full_like(q, nan)
+    lse = torch.full((4, q.shape[0]), nan, device=DEV)
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(v, nan)
+    say("varlen one side empty", side)
+    fa.fa_fwd_varlen(q, k, v, cq, ck, c.max_seqlen_q, c.max_seqlen_k, out=out, lse=lse, scale=c.scale)
+    fa.fa_bwd_varlen(q, k, v, out, do, lse, cq, ck, c.max_seqlen_q, c.max_seqlen_k, dq=dq, dk=dk, dv=dv,
+                     scale=c.scale)
+    torch.cuda.synchronize()
+    if side == "no_keys":
+        assert (out == 0).all() and torch.isposinf(lse).all() and (dq == 0).all()
+    else:
+        assert (dk == 0).all() and (dv == 0).all()
+
+
 def test_cfg4_full_size_sampled():
+    """Every sequence, every head: O, LSE and dQ on one seeded row of every
+    128-row query tile (plus first and last rows); dK/dV on one seeded key of
+    every 256-key block for one head per sequence."""
     c = cfg4()
     say("varlen", c.name)
     out, lse, (dq, dk, dv) = _run(c)
+    o_g, l_g, dq_g, dk_g, dv_g = (np64(x) for x in (out, lse, dq, dk, dv))
     cq = c.cu_seqlens_q.tolist()
-    for s in (0, 7, len(cq) - 2):
+    H = c.q.shape[1]
+    for s in range(len(cq) - 1):
         a, b = cq[s], cq[s + 1]
         L = b - a
-        rows = sorted(set([0, 1, L // 2, L - 1]))
         qs, ks, vs, ds = (t[a:b][None] for t in (c.q, c.k, c.v, c.dout))
-        heads = [0, 15]
-        ro, rl = attention_fwd(qs, ks, vs, c.scale, True, heads=heads, q_rows=rows)
-        o_g = out[a:b][None]
-        l_g = lse[:, a:b][None]
-        m_o = np.zeros(ro.shape, bool)
-        m_l = np.zeros(rl.shape, bool)
-        for h in heads:
-            m_o[:, rows, h, :] = True
-            m_l[:, h, rows] = True
-        assert_out(o_g, ro, torch.bfloat16, mask=m_o)
-        assert_lse(l_g, rl, mask=m_l)
-        gq, _, _ = attention_bwd(qs, ks, vs, ds, c.scale, True, heads=heads, q_rows=rows)
-        assert_grad(dq[a:b][None], gq, "dq", mask=m_o)
-        _, gk, gv = attention_bwd(qs, ks, vs, ds, c.scale, True, heads=heads, k_rows=rows)
-        assert_grad(dk[a:b][None], gk, "dk", mask=m_o)
-        assert_grad(dv[a:b][None], gv, "dv", mask=m_o)
+        for h in range(H):
+            rows = tile_rows(L, 128, 4000 + 100 * s + h)
+            ro, rl = attention_fwd(qs, ks, vs, c.scale, True, heads=[h], q_rows=rows)
+            ar = np.asarray(rows) + a
+            assert_out(o_g[ar, h], ro[0, rows, h], torch.bfloat16, what=f"out seq {s} head {h}")
+            assert_lse(l_g[h, ar], rl[0, h, rows], what=f"lse seq {s} head {h}")
+            gq, _, _ = attention_bwd(qs, ks, vs, ds, c.scale, True, heads=[h], q_rows=rows)
+            assert_grad(dq_g[ar, h], gq[0, rows, h], f"dq seq {s} head {h}")
+        h = s % H
+        keys = tile_rows(L, 256, 4500 + s)
+        _, gk, gv = attention_bwd(qs, ks, vs, ds, c.scale, True, heads=[h], k_rows=keys)
+        ak = np.asarray(keys) + a
+        assert_grad(dk_g[ak, h], gk[0, keys, h], f"dk seq {s} head {h}")
+        assert_grad(dv_g[ak, h], gv[0, keys, h], f"dv seq {s} head {h}")
 
 
 def test_sequence_isolation_bitwise():
