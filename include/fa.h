@@ -55,7 +55,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* a size, pointer, option or alignment is invalid */
   FA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for (e.g. D = 80) */
   FA_ERR_WORKSPACE = 3,   /* workspace pointer NULL or smaller than the size query */
-  FA_ERR_LAUNCH = 4       /* hipGetLastError reported an error after a launch */
+  FA_ERR_LAUNCH = 4,      /* hipGetLastError reported an error after a launch */
+  FA_ERR_SCRATCH_LIMIT = 5 /* fa_fwd_kvcache_noalloc: partials exceed its static scratch */
 } fa_status;
 
 typedef enum { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
@@ -296,6 +297,38 @@ int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_new,
  * and LSE_s (B,Hq,Sq_new,num_splits), or 0 when num_splits == 1; num_splits == 0
  * returns the size for 32 splits, enough for any automatic choice. */
 size_t fa_kvcache_workspace_size(int B, int Sq_new, int Hq, int D, int num_splits);
+
+/*
+ * fa_fwd_kvcache without a workspace argument, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * semantics and results as fa_fwd_kvcache (the same kernels run); the split
+ * partials go to a static device array of fa_kvcache_noalloc_max_bytes()
+ * bytes (8 MiB) that the library holds on each GPU it runs on until the
+ * process ends.  The call allocates nothing and calls no allocating routine;
+ * on the first call on a device it looks up that device's copy of the array
+ * (hipGetSymbolAddress) and keeps the address.
+ *   The current device must be the device of `stream` and of the tensors.
+ *   Returns FA_ERR_SCRATCH_LIMIT when fa_kvcache_workspace_size(B, Sq_new,
+ *   Hq, D, splits) exceeds the array, with splits = num_splits or, for
+ *   num_splits == 0, the library's automatic choice (e.g. D = 128:
+ *   B * Sq_new * Hq * splits <= 16256).
+ *   Every call on a GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (different streams, or several host threads) race and must be
+ *   ordered by the caller.  The array needs no clearing: each call writes
+ *   every partial it reads.
+ */
+int fa_fwd_kvcache_noalloc(const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int* cache_seqlens,
+                           const int* block_table, int max_blocks_per_seq, int page_size,
+                           const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                           void* out, float* lse,
+                           int B, int Sq_new, int Hq, int Hkv, int D, int dtype,
+                           float scale, int causal, int window_left, int window_right, float softcap,
+                           const float* alibi_slopes, int num_splits, void* stream);
+
+/* Bytes of the static scratch array behind fa_fwd_kvcache_noalloc. */
+size_t fa_kvcache_noalloc_max_bytes(void);
 
 /*
  * Kernel timing (for benchmarks and profiles).  When enabled, every kernel

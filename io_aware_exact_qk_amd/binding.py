@@ -92,6 +92,11 @@ def lib():
                                  _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
     L.fa_kvcache_workspace_size.restype = _Z
     L.fa_kvcache_workspace_size.argtypes = [_I] * 5
+    # the same arguments without (workspace, workspace_bytes)
+    L.fa_fwd_kvcache_noalloc.restype = _I
+    L.fa_fwd_kvcache_noalloc.argtypes = L.fa_fwd_kvcache.argtypes[:27] + [_P]
+    L.fa_kvcache_noalloc_max_bytes.restype = _Z
+    L.fa_kvcache_noalloc_max_bytes.argtypes = []
     L.fa_profiler_enable.restype = _I
     L.fa_profiler_enable.argtypes = [_I, _I]
     L.fa_profiler_reset.restype = _I
@@ -400,7 +405,7 @@ def fa_bwd_varlen_dropout(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, m
 def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, block_table=None,
                    rotary_cos=None, rotary_sin=None, rotary_dim=None, num_splits=1, out=None,
                    lse=None, scale=None, causal=True, window=(-1, -1), softcap=0.0,
-                   alibi_slopes=None, workspace=None, stream=None):
+                   alibi_slopes=None, workspace=None, stream=None, _noalloc=False):
     """Decode step: appends k_new/v_new in place, returns (out (B,Sq,Hq,D), lse (B,Hq,Sq))."""
     _check(q, "q", ndim=4)
     _check(k_cache, "k_cache", q.dtype, 4)
@@ -428,17 +433,29 @@ def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, b
     out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
     lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
     L = lib()
+    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+            _ptr(block_table), max_blocks, page, _ptr(rotary_cos), _ptr(rotary_sin), rd, _ptr(out), _ptr(lse),
+            B, Sq, Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes),
+            int(num_splits)]
+    if _noalloc:
+        _raise("fa_fwd_kvcache_noalloc", L.fa_fwd_kvcache_noalloc(*args, _stream(stream)))
+        return out, lse
     ws_bytes = L.fa_kvcache_workspace_size(B, Sq, Hq, D, int(num_splits))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
-    scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
-    st = L.fa_fwd_kvcache(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                          _ptr(cache_seqlens), _ptr(block_table), max_blocks, page, _ptr(rotary_cos),
-                          _ptr(rotary_sin), rd, _ptr(out), _ptr(lse), B, Sq, Hq, Hkv, D, _dt(q), scale,
-                          int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes), int(num_splits),
-                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    st = L.fa_fwd_kvcache(*args, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _raise("fa_fwd_kvcache", st)
     return out, lse
+
+
+def fa_fwd_kvcache_noalloc(*args, **kw):
+    """fa_fwd_kvcache (same arguments, no workspace) through the entry point
+    without a workspace: the library's static per-GPU scratch holds the split
+    partials.  Pass `out` and `lse` to keep the call free of any allocation."""
+    if "workspace" in kw:
+        raise TypeError("fa_fwd_kvcache_noalloc takes no workspace")
+    return fa_fwd_kvcache(*args, _noalloc=True, **kw)
 
 
 # ------------------------------------------------------------- profiler ----

@@ -54,6 +54,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH_LIMIT: return "request exceeds the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }

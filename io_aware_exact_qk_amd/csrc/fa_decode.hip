@@ -35,6 +35,7 @@
 // partials (O_s normalised, LSE_s) that the combine kernel merges with
 //   M = max_s LSE_s,  LSE = M + ln sum_s e^{LSE_s - M},  O = sum_s e^{LSE_s - LSE} O_s.
 #include <algorithm>
+#include <mutex>
 
 #include "fa_device.h"
 #include "fa_host.h"
@@ -626,6 +627,31 @@ static int auto_splits(int B, int Hkv, int max_pages) {
   return (int)std::max<long long>(s, 1);
 }
 
+// ------------------------------------------------- no-allocation variant --
+// Split partials of fa_fwd_kvcache_noalloc live in this file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// uses its name as an address (on the host it is only a stand-in symbol):
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch` (NULL on error).
+static void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace fa
 
 using namespace fa;
@@ -712,4 +738,30 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
     case 128: return bf ? launch_decode<128, DT_BF16>(p, opts, s) : launch_decode<128, DT_F16>(p, opts, s);
     default: return FA_ERR_UNSUPPORTED;
   }
+}
+
+extern "C" size_t fa_kvcache_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int fa_fwd_kvcache_noalloc(const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int* cache_seqlens,
+                                      const int* block_table, int max_blocks_per_seq, int page_size,
+                                      const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                                      void* out, float* lse,
+                                      int B, int Sq_new, int Hq, int Hkv, int D, int dtype,
+                                      float scale, int causal, int window_left, int window_right,
+                                      float softcap, const float* alibi_slopes, int num_splits, void* stream) {
+  if (B < 1 || Sq_new < 1 || Hq < 1 || Hkv < 1 || D < 1 || num_splits < 0 || max_blocks_per_seq < 1)
+    return FA_ERR_INVALID_ARG;
+  const int ns = num_splits == 0 ? auto_splits(B, Hkv, max_blocks_per_seq) : num_splits;
+  const size_t need = fa_kvcache_workspace_size(B, Sq_new, Hq, D, ns);
+  if (need > kScratchBytes) return FA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr();
+    if (!ws) return FA_ERR_LAUNCH;
+  }
+  return fa_fwd_kvcache(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, max_blocks_per_seq,
+                        page_size, rotary_cos, rotary_sin, rotary_dim, out, lse, B, Sq_new, Hq, Hkv, D, dtype,
+                        scale, causal, window_left, window_right, softcap, alibi_slopes, ns, ws, kScratchBytes,
+                        stream);
 }

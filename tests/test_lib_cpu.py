@@ -120,3 +120,16 @@ def test_varlen_rejects(lib):
     assert st == 1  # nseq = 0
     st = lib.fa_fwd_varlen(F, F, F, F, F, None, F, 1, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, None)
     assert st == 1  # cu_seqlens_q missing
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch(lib):
+    """fa_fwd_kvcache_noalloc refuses, on the host, partials larger than its
+    static scratch (B * Sq_new * Hq * splits * (D + 1) * 4 bytes > 8 MiB)."""
+    assert lib.fa_kvcache_noalloc_max_bytes() == 8 << 20
+    assert lib.fa_status_string(5).startswith(b"request exceeds the static scratch")
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: the call is refused first
+    B, Sq, Hq, Hkv, D, splits = 64, 1, 64, 8, 128, 32
+    assert lib.fa_kvcache_workspace_size(B, Sq, Hq, D, splits) > (8 << 20)
+    st = lib.fa_fwd_kvcache_noalloc(p, None, None, p, p, p, p, 300, 256, None, None, 0, p, p,
+                                    B, Sq, Hq, Hkv, D, 1, 0.088, 1, -1, -1, 0.0, None, splits, None)
+    assert st == 5
