@@ -18,10 +18,9 @@ Printed as one JSON line, with
                  sequence length up to 4K);
   decode       — the paged KV-cache decode step (B = 8, Hq = 32, Hkv = 8,
                  D = 128, cache lengths ~ U[1K, 64K], page 256, rotary,
-                 1 / 4 / 16 / automatic splits) in HBM GB/s, each timed call
-                 preceded by an untimed 1 GiB scratch write so the caches
-                 are cold (the warm, back-to-back rate is reported beside
-                 it);
+                 1 / 4 / 16 / automatic splits) in HBM GB/s, cold: four
+                 independent cache pools read in rotation (warm and
+                 after-a-scratch-write rates are reported beside it);
   memory_vs_naive — extra device memory of one fa_fwd + fa_bwd against
                  naive attention (scores and softmax materialised, float32
                  autograd) at S = 2K and 4K of the sweep shape, for context.
@@ -421,65 +420,55 @@ def decode_bytes(L, B, Hq, Hkv, D_, page):
     return kv + small + bt
 
 
+DECODE_POOLS = 4  # independent copies of the paged cache, read in rotation
+
+
 def run_decode(args, torch, fa, splits=16):
     """Paged decode at num_splits 1, 4, `splits` and automatic (or only
-    --decode-splits N); with --cold-only every call, warm-up included, follows
-    a scratch write, and no back-to-back (warm) calls are made, so a profile
-    of the run holds cold calls only."""
+    --decode-splits N).
+
+    Cold protocol: DECODE_POOLS independent copies of the cache pool (1.15 GB
+    each) are read in rotation, so every call reads bytes that the previous
+    DECODE_POOLS - 1 calls (3.4 GB) have pushed out of the 256 MB Infinity
+    Cache and the L2s, and no unrelated dirty lines are left to be written
+    back during the call.  Reported beside it, for context: back-to-back calls
+    on one pool (warm) and calls that each follow an untimed 1 GiB scratch
+    write (that write's dirty lines are written back while the call reads, so
+    it measures the call plus up to a few hundred MB of write-back).
+    With --cold-only only rotated calls are made (warm-up included), so a
+    profile of the run holds cold calls only."""
     from workloads import cfg5
     dev = torch.device("cuda:0")
     c = cfg5()
-    q, kc, vc = c.q.to(dev), c.k_cache.to(dev), c.v_cache.to(dev)
+    q = c.q.to(dev)
+    pools = [(c.k_cache.to(dev), c.v_cache.to(dev)) for _ in range(DECODE_POOLS)]
     kn, vn = c.k_new.to(dev), c.v_new.to(dev)
     sl, bt = c.cache_seqlens.to(dev), c.block_table.to(dev)
     cos, sin = c.rotary_cos.to(dev), c.rotary_sin.to(dev)
     out = torch.empty_like(q)
     lse = torch.empty(8, 32, 1, device=dev, dtype=torch.float32)
-    # Cold protocol: a 1 GiB scratch write before every timed call (outside
-    # the timed events) evicts the 256 MB Infinity Cache and the L2s, so the
-    # rate is that of a stream read from HBM.  Back-to-back calls re-read the
-    # same 1.1 GB and keep part of it in the Infinity Cache; that warm rate is
-    # reported beside it for context only.
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scratch = None if args.cold_only else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
     res = {}
     # 0 = the library's automatic choice
     split_list = [args.decode_splits] if args.decode_splits is not None else (
         [1, 4, splits, 0] if splits not in (1, 4, 0) else [1, 4, 0])
-    for ns in split_list:
-        ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
-                         dtype=torch.uint8)
+    reps = max(12, args.steps * 6)
 
-        def call():
-            fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
-                              scale=c.scale, workspace=ws)
-        for i in range(5):
-            if args.cold_only:
-                scratch.fill_(i & 255)
-            call()
-        torch.cuda.synchronize()
-        reps = max(10, args.steps * 5)
-        wall = warm_split_ms = float("nan")
-        if not args.cold_only:
-            fa.profiler_enable(1024)
-            fa.profiler_reset()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                call()
-            torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) / reps
-            prof = fa.profiler_read()
-            fa.profiler_disable()
-            warm_split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
-        # cold: every timed call follows the scratch write
-        fa.profiler_enable(1024)
+    def timed(ns, ws, pool_of, before=None):
+        """Median call time (HIP events) and mean split/combine kernel times
+        over `reps` calls; call i reads pool pool_of(i)."""
+        fa.profiler_enable(4 * reps)
         fa.profiler_reset()
         evs = []
         for i in range(reps):
-            scratch.fill_(i & 255)
+            if before is not None:
+                before(i)
+            kc, vc = pools[pool_of(i)]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            call()
+            fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
+                              scale=c.scale, workspace=ws)
             e1.record()
             evs.append((e0, e1))
         torch.cuda.synchronize()
@@ -487,24 +476,44 @@ def run_decode(args, torch, fa, splits=16):
         prof = fa.profiler_read()
         fa.profiler_disable()
         split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
-        comb_ms = prof["decode_combine"][0] / max(1, prof["decode_combine"][1]) if prof["decode_combine"][1] else 0.0
-        res[ns] = {"num_splits": ns, "us_per_call": round(call_ms * 1e3, 1),
-                   "GBps": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
-                   "split_kernel_us": round(split_ms * 1e3, 1), "combine_kernel_us": round(comb_ms * 1e3, 1),
-                   "split_kernel_GBps": round(nbytes / (split_ms * 1e-3) / 1e9, 1),
-                   "split_kernel_avg_us_all_launches": round(split_ms * 1e3, 2),
-                   "warm_us_per_call": None if args.cold_only else round(wall * 1e6, 1),
-                   "warm_GBps": None if args.cold_only else round(nbytes / wall / 1e9, 1),
-                   "warm_split_kernel_GBps": None if args.cold_only else round(nbytes / (warm_split_ms * 1e-3) / 1e9, 1)}
-        log(f"decode splits={ns}: {res[ns]}")
+        comb_ms = prof["decode_combine"][0] / prof["decode_combine"][1] if prof["decode_combine"][1] else 0.0
+        return call_ms, split_ms, comb_ms
+
+    for ns in split_list:
+        ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
+                         dtype=torch.uint8)
+        rot = lambda i: i % DECODE_POOLS
+        for i in range(2 * DECODE_POOLS):  # warm-up (rotated)
+            kc, vc = pools[rot(i)]
+            fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
+                              scale=c.scale, workspace=ws)
+        torch.cuda.synchronize()
+        call_ms, split_ms, comb_ms = timed(ns, ws, rot)
+        r = {"num_splits": ns, "us_per_call": round(call_ms * 1e3, 1),
+             "GBps": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+             "split_kernel_us": round(split_ms * 1e3, 2), "combine_kernel_us": round(comb_ms * 1e3, 2),
+             "split_kernel_GBps": round(nbytes / (split_ms * 1e-3) / 1e9, 1)}
+        if not args.cold_only:
+            w_call, w_split, _ = timed(ns, ws, lambda i: 0)
+            f_call, f_split, _ = timed(ns, ws, lambda i: 0, before=lambda i: scratch.fill_(i & 255))
+            r.update({"warm_us_per_call": round(w_call * 1e3, 1), "warm_GBps": round(nbytes / w_call / 1e6, 1),
+                      "warm_split_kernel_GBps": round(nbytes / w_split / 1e6, 1),
+                      "after_write_flush_us_per_call": round(f_call * 1e3, 1),
+                      "after_write_flush_GBps": round(nbytes / f_call / 1e6, 1),
+                      "after_write_flush_split_kernel_GBps": round(nbytes / f_split / 1e6, 1)})
+        res[ns] = r
+        log(f"decode splits={ns}: {r}")
     best = max(res.values(), key=lambda r: r["GBps"])
     return {"workload": "decode bf16 B=8 Hq=32 Hkv=8 D=128 page=256 rotary128, cache_seqlens seed 5",
-            "timing": "cold: 1 GiB scratch write before each timed call (untimed); warm_*: back-to-back calls",
+            "timing": f"cold: {DECODE_POOLS} independent cache pools read in rotation (HIP events, median "
+                      f"call; kernel means); warm_*: back-to-back calls on one pool; after_write_flush_*: each "
+                      "call after an untimed 1 GiB scratch write",
             "bytes_per_call": nbytes, "best": best, "by_splits": list(res.values()),
             "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": best["split_kernel_GBps"],
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(best["split_kernel_GBps"] / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_split")}}
+                         "traffic": recorded_traffic("decode_split"),
+                         "avg_launch_us": best["split_kernel_us"], "bytes_per_launch": nbytes}}
 
 
 # ---------------------------------------------------------------------------

@@ -206,9 +206,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     };
 
     // Logits of tile t in the log2 domain (up to the folded scale fs), masked
-    // entries at -inf (keys past Sk hold a copy of the last key), then the
-    // lazy online-softmax update of the exponent reference.  Returns m_use.
-    auto prep = [&](int t, f32x16 (&sa)[2]) -> float {
+    // entries at -inf (keys past Sk hold a copy of the last key).
+    auto logits = [&](int t, f32x16 (&sa)[2]) {
       const int j0 = t * BC;
       if constexpr (SOFTCAP || ALIBI) {
 #pragma unroll
@@ -235,15 +234,15 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
           }
         }
       }
-      // The exponent reference m_run moves only when the tile max exceeds it
-      // by more than kRescaleSlack; until then p <= 2^kRescaleSlack, which the
-      // float32 sums and the 16-bit P operand carry without loss, and the
-      // rescale of O (64 multiplies per lane) is skipped.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[kb][i]);
+    };
+
+    // Lazy online-softmax update of the exponent reference from this lane's
+    // tile maximum mx (before the lane-half exchange and the folded scale).
+    // The reference m_run moves only when the tile max exceeds it by more
+    // than kRescaleSlack; until then p <= 2^kRescaleSlack, which the float32
+    // sums and the 16-bit P operand carry without loss, and the rescale of O
+    // (64 multiplies per lane) is skipped.  Returns m_use.
+    auto rescale = [&](float mx) -> float {
       mx = pair_max32(mx) * fs;
       if (__any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
@@ -256,6 +255,16 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       return (m_run == -INFINITY) ? 0.0f : m_run;
     };
 
+    auto prep = [&](int t, f32x16 (&sa)[2]) -> float {
+      logits(t, sa);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[kb][i]);
+      return rescale(mx);
+    };
+
     // Dropout keep words of tile t (two 32-key halves).
     auto keepw = [&](int t, uint32_t (&kw)[2][4]) {
       if constexpr (DROP) {
@@ -264,19 +273,21 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       }
     };
 
-    // P = 2^(x - m) as four 16-bit B operands (acc-order), row sums into l_run
-    // (dropped weights count in the sum and enter the product as 0).
+    // P = 2^(x - m) as four 16-bit B operands (acc-order), row sums of the
+    // float32 weights into l_run (dropped weights count in the sum and enter
+    // the product as 0).
     auto expo = [&](f32x16 (&sa)[2], float m_use, const uint32_t (&kw)[2][4], u32x4 (&pb)[4]) {
-      float lsum = 0.0f;
+      float lsum = 0.0f, lsum2 = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = fast_exp2(fmaf(sa[kb][i], fs, -m_use));
-          lsum += pv;
+          if (i & 1) lsum2 += pv;
+          else lsum += pv;
           sa[kb][i] = (DROP && !drop_keep(kw[kb], i, p.drop.t)) ? 0.0f : pv;
         }
-      l_run += lsum;
+      l_run += lsum + lsum2;
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk) pb[mk] = pack_frag_half<DT>(sa[mk >> 1], mk & 1);
     };
@@ -301,8 +312,9 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
 
     // The pipelined block in an explicit instruction order.  S of the next
     // tile: a ring of four K fragments keeps four LDS reads in flight ahead of
-    // the MFMA that consumes them, and each MFMA is followed by a slice of the
-    // current tile's exponentials; once the K ring has nothing left to fetch,
+    // the MFMA that consumes them; the first MXS MFMAs carry the current
+    // tile's maximum and the exponent-reference update, each later one a
+    // slice of the current tile's exponentials; once the K ring has nothing left to fetch,
     // its last slots start the first three V^T fragments.  Then O += P V with
     // a ring of three V^T fragments (six transposed reads) in flight, with
     // the packing of P and the row sum spread over those MFMAs, so the
@@ -311,16 +323,18 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
     // from pulling each read down next to its MFMA, which would expose the
     // whole LDS latency on every MFMA.
     auto fused = [&](const char* kn, const char* vt, uint32_t nbv, uint32_t tbv, u32x4 (&kr)[4],
-                     f32x16 (&sc)[2], f32x16 (&sn)[2], float m_use, const uint32_t (&kw)[2][4]) {
+                     f32x16 (&sc)[2], f32x16 (&sn)[2]) {
       constexpr int NS = 2 * KC;    // S MFMAs per tile
-      constexpr int EPS = 32 / NS;  // softmax elements per S MFMA
+      constexpr int MXS = 2;        // S MFMAs that carry the tile maximum
       constexpr int NP = 4 * DB;    // P V MFMAs per tile
       constexpr int LEAD = DB >= 2 ? 2 : 1;
       sn[0] = f32x16{};
       sn[1] = f32x16{};
-      float lsum = 0.0f;
+      float lsum = 0.0f, lsum2 = 0.0f;
+      float mx = -INFINITY, m_use = 0.0f;
       u32x4 pb[4];
       u32x4 vr[3];
+      bool pb0 = false;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int kb = i / KC, c = i % KC;
@@ -331,14 +345,24 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
           const int j = i + 4 - NS;
           vr[j] = lds_At<D>(vt + (16 * (j / DB)) * (D * 2), tbv, j % DB);
         }
+        if (i < MXS) {
+          // the tile maximum of the current tile, under the first S MFMAs of
+          // the next one (they do not depend on it)
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) {
-          const int idx = i * EPS + e;
-          sc[idx >> 4][idx & 15] = fast_exp2(fmaf(sc[idx >> 4][idx & 15], fs, -m_use));
+          for (int e = 32 * i / MXS; e < 32 * (i + 1) / MXS; ++e) mx = fmaxf(mx, sc[e >> 4][e & 15]);
+        } else {
+          if (i == MXS) m_use = rescale(mx);
+          // the current tile's exponentials, spread over the remaining S MFMAs
+#pragma unroll
+          for (int e = 32 * (i - MXS) / (NS - MXS); e < 32 * (i - MXS + 1) / (NS - MXS); ++e)
+            sc[e >> 4][e & 15] = fast_exp2(fmaf(sc[e >> 4][e & 15], fs, -m_use));
+          // the first P operand is packed once its eight weights exist; the
+          // other three, and the row sum, go under the P V MFMAs
+          if (!pb0 && 32 * (i - MXS + 1) / (NS - MXS) >= 8) {
+            pb[0] = pack_frag_half<DT>(sc[0], 0);
+            pb0 = true;
+          }
         }
-        // the first P operand is packed here; the other three, and the row
-        // sum, under the P V MFMAs, which carry no other element-wise work
-        if ((i + 1) * EPS == 8) pb[0] = pack_frag_half<DT>(sc[0], 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -350,11 +374,20 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
 #pragma unroll
         for (int mn = 1; mn < 4; ++mn)
           if (i == mn * DB - LEAD) pb[mn] = pack_frag_half<DT>(sc[mn >> 1], mn & 1);
+        // row sum of the float32 weights (the LSE needs their exact sum, not
+        // that of the 16-bit P operand), two chains
 #pragma unroll
-        for (int e = i * 32 / NP; e < (i + 1) * 32 / NP; ++e) lsum += sc[e >> 4][e & 15];
+        for (int e = i * 32 / NP; e < (i + 1) * 32 / NP; ++e) {
+          if (e & 1) lsum2 += sc[e >> 4][e & 15];
+          else lsum += sc[e >> 4][e & 15];
+        }
+        // pin the partial sums here (an empty asm that reads and redefines
+        // them), so they run under this MFMA instead of being sunk after the
+        // block as one serial chain
+        asm volatile("" : "+v"(lsum), "+v"(lsum2));
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += lsum;
+      l_run += lsum + lsum2;
     };
 
     // Pipelined step for tile t (t + 1 < t_hi): `sc` holds S of tile t, the
@@ -369,10 +402,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       const uint32_t nbv = opaque(nb), tbv = opaque(tb);
       u32x4 kr[4];
       k_ring(kn, nbv, kr);
-      uint32_t kw[2][4];
-      keepw(t, kw);
-      const float m_use = prep(t, sc);
-      fused(kn, vt, nbv, tbv, kr, sc, sn, m_use, kw);
+      logits(t, sc);
+      fused(kn, vt, nbv, tbv, kr, sc, sn);
       dma_wait();
       __syncthreads();
     };
