@@ -350,11 +350,15 @@ def run_configs(args, torch, fa):
     pairs = 16 * sum(pairs_causal(L) for L in lens)
     out, lse = torch.empty_like(q), torch.empty(16, q.shape[0], device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.lib().fa_bwd_varlen_workspace_size(q.shape[0], 16, 128, 0), device=dev, dtype=torch.uint8)
+    nseq = len(lens)
+    ws = torch.empty(fa.lib().fa_bwd_varlen_workspace_size(nseq, q.shape[0], k.shape[0], 16, 128, 0), device=dev,
+                     dtype=torch.uint8)
+    wsf = torch.empty(fa.lib().fa_fwd_varlen_workspace_size(nseq, q.shape[0], 16, 128), device=dev,
+                      dtype=torch.uint8)
     mq, mk = c.max_seqlen_q, c.max_seqlen_k
 
     def f4():
-        fa.fa_fwd_varlen(q, k, v, cq, ck, mq, mk, out=out, lse=lse, scale=c.scale, causal=True)
+        fa.fa_fwd_varlen(q, k, v, cq, ck, mq, mk, out=out, lse=lse, scale=c.scale, causal=True, workspace=wsf)
 
     def fb4():
         f4()

@@ -108,17 +108,27 @@ size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int 
  * batches of sequences with different lengths use the varlen interface).
  *   q/out/dout/dq (total_q, Hq, D); k/v/dk/dv (total_k, Hkv, D); lse (Hq, total_q).
  *   cu_seqlens_q/k: int32 device arrays (nseq + 1), prefix sums of lengths.
- *   max_seqlen_q/k: upper bounds of the per-sequence lengths (sizes the grid).
+ *   max_seqlen_q/k: upper bounds of the per-sequence lengths.
  * Sequence s is attention over rows [cu_q[s], cu_q[s+1]) x [cu_k[s], cu_k[s+1]),
  * independent of every other sequence.  dk/dv rows that belong to no
  * sequence are left untouched.
+ * Scheduling: a small kernel first writes, into the workspace, the list of
+ * the real (sequence, tile) pairs from cu_seqlens (on the device, no host
+ * synchronisation), level by level so that the heaviest tiles of a causal
+ * launch come first; the attention kernels then run one work-group per
+ * (list entry, head) and no work-group for tiles past a sequence's end.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
                   int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                   int Hq, int Hkv, int D, int dtype,
                   float scale, int causal, int window_left, int window_right, float softcap,
-                  const float* alibi_slopes, void* stream);
+                  const float* alibi_slopes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for fa_fwd_varlen: the tile list, 8 bytes per entry for at
+ * most (total_q + 127 nseq) / 128 entries, padded to 256 bytes (0 when
+ * total_q == 0, and the pointer may then be NULL). */
+size_t fa_fwd_varlen_workspace_size(int nseq, int total_q, int Hq, int D);
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv,
@@ -129,9 +139,10 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* out, 
                   const float* alibi_slopes, int deterministic,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace for fa_bwd_varlen: two float32 (Hq, total_q) row arrays, each
- * padded to 256 bytes. */
-size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic);
+/* Workspace for fa_bwd_varlen: two float32 (Hq, total_q) row arrays, then
+ * the list of 128-row query tiles (for dQ) and the list of key tiles (256
+ * keys; 128 at D = 256, for dK/dV), each padded to 256 bytes. */
+size_t fa_bwd_varlen_workspace_size(int nseq, int total_q, int total_k, int Hq, int D, int deterministic);
 
 /*
  * Packed layouts (section "上手 FlashAttention 的三步走": when Q, K and V are
@@ -229,7 +240,7 @@ int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* out
                           int Hq, int Hkv, int D, int dtype,
                           float scale, int causal, int window_left, int window_right, float softcap,
                           const float* alibi_slopes, float dropout_p, unsigned long long seed,
-                          unsigned long long offset, void* stream);
+                          unsigned long long offset, void* workspace, size_t workspace_bytes, void* stream);
 
 int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* out,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,

@@ -55,12 +55,14 @@ def lib():
     L.fa_bwd_workspace_size.argtypes = [_I] * 7
     L.fa_fwd_varlen.restype = _I
     L.fa_fwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
-                                _I, _I, _F, _P, _P]
+                                _I, _I, _F, _P, _P, _Z, _P]
+    L.fa_fwd_varlen_workspace_size.restype = _Z
+    L.fa_fwd_varlen_workspace_size.argtypes = [_I] * 4
     L.fa_bwd_varlen.restype = _I
     L.fa_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _I, _I, _I, _F, _P, _I, _P, _Z, _P]
     L.fa_bwd_varlen_workspace_size.restype = _Z
-    L.fa_bwd_varlen_workspace_size.argtypes = [_I] * 4
+    L.fa_bwd_varlen_workspace_size.argtypes = [_I] * 6
     # dropout variants: the plain argument list with (p, seed, offset) in
     # front of the stream (forward) or of `deterministic` (backward)
     _D = [_F, ctypes.c_ulonglong, ctypes.c_ulonglong]
@@ -69,7 +71,7 @@ def lib():
     L.fa_bwd_dropout.restype = _I
     L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:22] + _D + L.fa_bwd.argtypes[22:]
     L.fa_fwd_varlen_dropout.restype = _I
-    L.fa_fwd_varlen_dropout.argtypes = L.fa_fwd_varlen.argtypes[:-1] + _D + [_P]
+    L.fa_fwd_varlen_dropout.argtypes = L.fa_fwd_varlen.argtypes[:-3] + _D + [_P, _Z, _P]
     L.fa_fwd_qkvpacked.restype = _I
     L.fa_fwd_qkvpacked.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _P]
     L.fa_bwd_qkvpacked.restype = _I
@@ -332,7 +334,7 @@ def fa_fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, out=None
 # --------------------------------------------------------------- varlen ----
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out=None,
                   lse=None, scale=None, causal=False, window=(-1, -1), softcap=0.0,
-                  alibi_slopes=None, stream=None, _dropout=None):
+                  alibi_slopes=None, workspace=None, stream=None, _dropout=None):
     """Packed q (total_q,Hq,D), k/v (total_k,Hkv,D) -> (out, lse (Hq,total_q))."""
     _check(q, "q", ndim=3)
     _check(k, "k", q.dtype, 3)
@@ -347,13 +349,17 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     out = torch.empty_like(q) if out is None else _check(out, "out", q.dtype)
     lse = torch.empty(Hq, tq, device=q.device, dtype=torch.float32) if lse is None else _check(lse, "lse", torch.float32)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)
+    ws_bytes = lib().fa_fwd_varlen_workspace_size(nseq, tq, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
             _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
             Hq, Hkv, D, _dt(q), scale, int(bool(causal)), wl, wr, sc, _ptr(alibi_slopes)]
+    ws = [_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)]
     if _dropout is None:
-        _raise("fa_fwd_varlen", lib().fa_fwd_varlen(*args, _stream(stream)))
+        _raise("fa_fwd_varlen", lib().fa_fwd_varlen(*args, *ws))
     else:
-        _raise("fa_fwd_varlen_dropout", lib().fa_fwd_varlen_dropout(*args, *_dropout, _stream(stream)))
+        _raise("fa_fwd_varlen_dropout", lib().fa_fwd_varlen_dropout(*args, *_dropout, *ws))
     return out, lse
 
 
@@ -377,7 +383,7 @@ def fa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     dk = torch.zeros_like(k) if dk is None else _check(dk, "dk", q.dtype)
     dv = torch.zeros_like(v) if dv is None else _check(dv, "dv", q.dtype)
     L = lib()
-    ws_bytes = L.fa_bwd_varlen_workspace_size(tq, Hq, D, int(bool(deterministic)))
+    ws_bytes = L.fa_bwd_varlen_workspace_size(nseq, tq, tk, Hq, D, int(bool(deterministic)))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
     scale, wl, wr, sc = _opts(D, scale, window, softcap, alibi_slopes)

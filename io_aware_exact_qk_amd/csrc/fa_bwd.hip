@@ -52,6 +52,7 @@ struct BwdParams {
   const float* alibi;
   int wl, wr;
   int n_tiles, n_heads, n_batch, reverse, balanced;
+  const int* tiles;  // varlen tile list (entries x 2 ints), or NULL
   DropSpec drop; // DROP kernels only
 };
 
@@ -142,7 +143,12 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
   // causal: the first key tiles are seen by the most queries
-  const TileId tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, false);
+  TileId tid3;
+  if (p.tiles) {
+    if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
+  } else {
+    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, false);
+  }
   const int tk = tid3.t, hk = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
   const int k0 = tk * BC;
@@ -389,7 +395,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   const uint32_t nb = nat_base<D>(lane);
   const uint32_t tb = tr_base<D>(lane);
   // causal: the last query tiles see the most keys
-  const TileId tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, p.reverse != 0);
+  TileId tid3;
+  if (p.tiles) {
+    if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
+  } else {
+    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, p.reverse != 0);
+  }
   const int tq = tid3.t, h = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
   const int q0 = tq * BR;
@@ -626,24 +637,34 @@ static void launch_all(const BwdParams& dkdv, const BwdParams& dq, int nwg_kv, i
   }
 }
 
+// Keys per dK/dV work-group.
+inline int dkdv_keys(int D) { return 32 * (D >= 256 ? DkdvShape<256>::NW : DkdvShape<128>::NW); }
+
+// Varlen launches pass their tile lists (q_list: 128-row query tiles for dQ,
+// kv_list: dK/dV key tiles) with their entry counts; the grids then run one
+// work-group per (entry, head).
 static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int max_sk, int nbatch,
-                   int causal, hipStream_t st) {
+                   int causal, hipStream_t st, const int* q_list = nullptr, long long q_entries = 0,
+                   const int* kv_list = nullptr, long long kv_entries = 0) {
   if (causal) base.wr = 0;
+  if (q_entries > 0x7fffffffLL || kv_entries > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   BwdParams kv = base;
-  const int kv_keys = 32 * (D >= 256 ? DkdvShape<256>::NW : DkdvShape<128>::NW);
-  kv.n_tiles = (max_sk + kv_keys - 1) / kv_keys;
+  const int kv_keys = dkdv_keys(D);
+  kv.tiles = kv_list;
+  kv.n_tiles = kv_list ? (int)kv_entries : (max_sk + kv_keys - 1) / kv_keys;
   kv.n_heads = Hkv;
-  kv.n_batch = nbatch;
+  kv.n_batch = kv_list ? 1 : nbatch;
   kv.reverse = 0;
   kv.balanced = causal ? 1 : 0;
   BwdParams dq = base;
-  dq.n_tiles = (max_sq + 127) / 128;
+  dq.tiles = q_list;
+  dq.n_tiles = q_list ? (int)q_entries : (max_sq + 127) / 128;
   dq.n_heads = base.Hq;
-  dq.n_batch = nbatch;
+  dq.n_batch = q_list ? 1 : nbatch;
   dq.reverse = causal ? 1 : 0;
   dq.balanced = causal ? 1 : 0;
-  const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * nbatch;
-  const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * nbatch;
+  const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * kv.n_batch;
+  const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * dq.n_batch;
   if (nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const bool sc = base.cap_log2 > 0.0f, al = base.alibi != nullptr;
   const bool bf = dtype == FA_DTYPE_BF16;
@@ -721,11 +742,19 @@ extern "C" size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, 
   return 2 * align_up((size_t)B * Hq * Sq * sizeof(float), 256);
 }
 
-extern "C" size_t fa_bwd_varlen_workspace_size(int total_q, int Hq, int D, int deterministic) {
-  (void)D;
+// Row-term arrays, then the query-tile list, then the key-tile list.
+static size_t bwd_varlen_rows_bytes(int total_q, int Hq) {
+  return align_up((size_t)total_q * Hq * sizeof(float), 256);
+}
+
+extern "C" size_t fa_bwd_varlen_workspace_size(int nseq, int total_q, int total_k, int Hq, int D,
+                                               int deterministic) {
   (void)deterministic;
-  if (total_q < 0 || Hq < 1) return 0;
-  return 2 * align_up((size_t)total_q * Hq * sizeof(float), 256);
+  if (nseq < 1 || total_q < 0 || total_k < 0 || Hq < 1) return 0;
+  size_t n = 2 * bwd_varlen_rows_bytes(total_q, Hq);
+  if (total_q > 0) n += varlen_list_bytes(total_q, nseq, 128);
+  if (total_k > 0) n += varlen_list_bytes(total_k, nseq, dkdv_keys(D));
+  return n;
 }
 
 // Row strides (elements between consecutive tokens) of q; k and v; dq;
@@ -779,7 +808,7 @@ static int bwd_varlen(const void* q, const void* k, const void* v, const void* o
                                      aligned4(lse));
   const bool k_ok = total_k == 0 || (aligned16(k) && aligned16(v) && aligned16(dk) && aligned16(dv));
   if (!q_ok || !k_ok || (alibi_slopes && !aligned4(alibi_slopes))) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_bwd_varlen_workspace_size(total_q, Hq, D, deterministic);
+  const size_t need = fa_bwd_varlen_workspace_size(nseq, total_q, total_k, Hq, D, deterministic);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
   if (total_q == 0 && total_k == 0) return FA_OK;
   // With keys but no queries the dK/dV kernel still runs and writes dK = dV = 0
@@ -790,13 +819,37 @@ static int bwd_varlen(const void* q, const void* k, const void* v, const void* o
   BwdParams p{};
   fill_common(p, q, k, v, out, dout, lse, dq, dk, dv, Hq, Hkv, D, scale, window_left, window_right, softcap,
               alibi_slopes);
-  p.dvec = (float*)workspace;
-  p.lse2 = (float*)((char*)workspace + need / 2);
+  const size_t rows = bwd_varlen_rows_bytes(total_q, Hq);
+  char* ws = (char*)workspace;
+  p.dvec = (float*)ws;
+  p.lse2 = (float*)(ws + rows);
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.drop = drop;
-  return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, causal, (hipStream_t)stream);
+  // tile lists: query tiles heaviest (last) first for causal; key tiles of
+  // a causal launch are heaviest first when taken from tile 0 up
+  hipStream_t s = (hipStream_t)stream;
+  int* q_list = nullptr;
+  int* kv_list = nullptr;
+  long long q_entries = 0, kv_entries = 0;
+  char* lists = ws + 2 * rows;
+  if (total_q > 0) {
+    q_list = (int*)lists;
+    q_entries = varlen_list_entries(total_q, nseq, 128);
+    lists += varlen_list_bytes(total_q, nseq, 128);
+    st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, q_list, q_entries, s);
+    if (st) return st;
+  }
+  if (total_k > 0) {
+    const int kk = dkdv_keys(D);
+    kv_list = (int*)lists;
+    kv_entries = varlen_list_entries(total_k, nseq, kk);
+    st = varlen_schedule(cu_seqlens_k, nseq, kk, (max_seqlen_k + kk - 1) / kk, causal != 0, kv_list, kv_entries, s);
+    if (st) return st;
+  }
+  return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, causal, s, q_list, q_entries, kv_list,
+                 kv_entries);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,

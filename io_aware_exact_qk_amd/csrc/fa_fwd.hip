@@ -48,6 +48,7 @@ struct FwdParams {
   int wl, wr;           // window, causal folded into wr = 0
   int n_qtiles, n_heads, n_batch;
   int reverse;          // causal: heaviest tiles first
+  const int* tiles;     // varlen tile list (entries x 2 ints), or NULL
   DropSpec drop;        // DROP kernels only
   // FP8 kernels: q and k are OCP e4m3 bytes, v the bfloat16 copy of the fp8
   // values; per-(batch, K/V head) dequantisation factors, NULL = 1
@@ -84,7 +85,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
 
   // logical tile id -> (q tile, head, batch)
   // causal: the last query tiles see the most keys
-  const TileId tid3 = tile_id(p.n_qtiles, p.n_heads, p.n_batch, p.reverse != 0, p.reverse != 0);
+  TileId tid3;
+  if (p.tiles) {
+    if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
+  } else {
+    tid3 = tile_id(p.n_qtiles, p.n_heads, p.n_batch, p.reverse != 0, p.reverse != 0);
+  }
   const int tq = tid3.t, h = tid3.h, b = tid3.b;
 
   int q_start, Sq, k_start, Sk;
@@ -547,15 +553,23 @@ static void launch_fwd_d(const FwdParams& prm, bool softcap, bool alibi, bool dr
 }
 
 static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap, int causal,
-                   int max_sq, int nbatch, hipStream_t st, bool fp8 = false) {
+                   int max_sq, int nbatch, hipStream_t st, bool fp8 = false, long long list_entries = 0) {
   prm.scale_log2 = scale * kLog2e;
   prm.scale_over_cap = softcap > 0.0f ? scale / softcap : 0.0f;
   prm.cap_log2 = softcap * kLog2e;
   if (causal) prm.wr = 0;
-  prm.n_qtiles = (max_sq + 127) / 128;
   prm.n_heads = prm.Hq;
-  prm.n_batch = nbatch;
+  if (prm.tiles) {
+    if (list_entries > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    prm.n_qtiles = (int)list_entries;
+    prm.n_batch = 1;
+  } else {
+    prm.n_qtiles = (max_sq + 127) / 128;
+    prm.n_batch = nbatch;
+  }
   prm.reverse = causal ? 1 : 0;
+  // a varlen tile list replaces the (tile, head, sequence) grid: n_qtiles
+  // then counts list entries and n_batch is 1
   const long long nwg = (long long)prm.n_qtiles * prm.n_heads * prm.n_batch;
   if (nwg <= 0) return FA_OK;
   if (nwg > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
@@ -591,6 +605,85 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
       break;
   }
   prof_after(FA_KERNEL_FWD, st);
+  return launch_status();
+}
+
+// ------------------------------------------------------ varlen tile list --
+// One work-group of 1024 threads writes the list (layout and order in
+// fa_host.h).  Levels are taken in passes of TP <= 1024; in a pass, thread
+// (lvl, c) owns level lvl and the c-th of 1024 / TP contiguous chunks of the
+// sequences: it counts the chunk's sequences with a tile at that level,
+// chunk counts and level totals give every (level, chunk) its first slot,
+// and it then writes the chunk's entries in sequence order.  Integer work
+// only; the list is the same on every call.
+__global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int* cu, int nseq, int tile, int levels,
+                                                              int ascending, int* list, int n_entries) {
+  __shared__ int cnt[1024];
+  __shared__ int ltot[1024];
+  __shared__ int lstart[1024];
+  __shared__ int sbase;
+  const int tid = threadIdx.x;
+  const int TP = levels < 1024 ? (levels > 0 ? levels : 1) : 1024;
+  const int C = 1024 / TP;
+  const int lvl = tid % TP, c = tid / TP;
+  const bool active = c < C;
+  const int CS = (nseq + C - 1) / C;
+  const int s0 = min(nseq, c * CS), s1 = min(nseq, s0 + CS);
+  auto ntiles = [&](int sq) {
+    const int len = cu[sq + 1] - cu[sq];
+    return len > 0 ? (len + tile - 1) / tile : 0;
+  };
+  int base = 0;
+  for (int L0 = 0; L0 < levels; L0 += TP) {
+    const int npass = min(TP, levels - L0);
+    const int k = L0 + lvl;
+    const int t = ascending ? k : levels - 1 - k;
+    const bool mine = active && lvl < npass;
+    int n = 0;
+    if (mine)
+      for (int sq = s0; sq < s1; ++sq) n += ntiles(sq) > t;
+    if (active) cnt[tid] = n;
+    __syncthreads();
+    if (tid < npass) {
+      int tt = 0;
+      for (int cc = 0; cc < C; ++cc) tt += cnt[cc * TP + tid];
+      ltot[tid] = tt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = base;
+      for (int l = 0; l < npass; ++l) {
+        lstart[l] = acc;
+        acc += ltot[l];
+      }
+      sbase = acc;
+    }
+    __syncthreads();
+    if (mine) {
+      int pos = lstart[lvl];
+      for (int cc = 0; cc < c; ++cc) pos += cnt[cc * TP + lvl];
+      for (int sq = s0; sq < s1; ++sq) {
+        if (ntiles(sq) > t) {
+          list[2 * pos] = sq;
+          list[2 * pos + 1] = t;
+          ++pos;
+        }
+      }
+    }
+    base = sbase;
+    __syncthreads();  // cnt and lstart are rewritten by the next pass
+  }
+  for (int e = base + tid; e < n_entries; e += 1024) {
+    list[2 * e] = -1;
+    list[2 * e + 1] = -1;
+  }
+}
+
+int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int* list,
+                    long long n_entries, hipStream_t st) {
+  if (n_entries > 0x3fffffffLL || levels < 0) return FA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, tile, levels,
+                     ascending ? 1 : 0, list, (int)n_entries);
   return launch_status();
 }
 
@@ -636,7 +729,8 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
                       int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                       int Hq, int Hkv, int D, int dtype,
                       float scale, int causal, int window_left, int window_right, float softcap,
-                      const float* alibi_slopes, const DropSpec& drop, void* stream) {
+                      const float* alibi_slopes, const DropSpec& drop, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int st = check_common(Hq, Hkv, D, dtype, scale, window_left, window_right, softcap);
   if (st) return st;
   if (nseq < 1 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
@@ -646,8 +740,16 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
   if (total_k > 0 && (!aligned16(k) || !aligned16(v))) return FA_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_fwd_varlen_workspace_size(nseq, total_q, Hq, D);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_WORKSPACE;
   if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  // the real (sequence, 128-row tile) pairs, heaviest level first
+  const long long entries = varlen_list_entries(total_q, nseq, 128);
+  st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, (int*)workspace, entries,
+                       (hipStream_t)stream);
+  if (st) return st;
   FwdParams prm{};
+  prm.tiles = (const int*)workspace;
   prm.q = (const uint16_t*)q;
   prm.k = (const uint16_t*)k;
   prm.v = (const uint16_t*)v;
@@ -665,7 +767,7 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
   prm.wl = window_left;
   prm.wr = window_right;
   prm.drop = drop;
-  return run_fwd(prm, D, dtype, scale, softcap, causal, max_seqlen_q, nseq, (hipStream_t)stream);
+  return run_fwd(prm, D, dtype, scale, softcap, causal, max_seqlen_q, nseq, (hipStream_t)stream, false, entries);
 }
 
 }  // namespace fa
@@ -762,15 +864,22 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, void* out
   return run_fwd(prm, D, FA_DTYPE_BF16, scale, softcap, causal, Sq, B, s, true);
 }
 
+extern "C" size_t fa_fwd_varlen_workspace_size(int nseq, int total_q, int Hq, int D) {
+  (void)Hq;
+  (void)D;
+  if (nseq < 1 || total_q < 1) return 0;
+  return varlen_list_bytes(total_q, nseq, 128);
+}
+
 extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                              const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
                              int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                              int Hq, int Hkv, int D, int dtype,
                              float scale, int causal, int window_left, int window_right, float softcap,
-                             const float* alibi_slopes, void* stream) {
+                             const float* alibi_slopes, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k,
                     total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left, window_right, softcap,
-                    alibi_slopes, DropSpec{}, stream);
+                    alibi_slopes, DropSpec{}, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -779,10 +888,11 @@ extern "C" int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v
                                      int Hq, int Hkv, int D, int dtype,
                                      float scale, int causal, int window_left, int window_right,
                                      float softcap, const float* alibi_slopes, float dropout_p,
-                                     unsigned long long seed, unsigned long long offset, void* stream) {
+                                     unsigned long long seed, unsigned long long offset, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   DropSpec drop;
   if (!make_drop(dropout_p, seed, offset, drop)) return FA_ERR_INVALID_ARG;
   return fwd_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k,
                     total_q, total_k, Hq, Hkv, D, dtype, scale, causal, window_left, window_right, softcap,
-                    alibi_slopes, drop, stream);
+                    alibi_slopes, drop, workspace, workspace_bytes, stream);
 }

@@ -87,6 +87,42 @@ __device__ __forceinline__ TileId tile_id(int n_tiles, int n_heads, int n_batch,
   return r;
 }
 
+// ---- varlen tile list (kernel in fa_fwd.hip) ----
+// A packed variable-length launch runs one work-group per (list entry, head)
+// instead of one per (max_seqlen tile, head, sequence): the list holds the
+// real (sequence, tile) pairs only, built on the device from cu_seqlens.
+// Entry e is the int pair list[2e] = sequence, list[2e + 1] = tile index
+// within it; unused trailing entries hold -1.  Order: level by level (tile
+// index t from the highest down, or from 0 up with ascending), sequences in
+// index order within a level, so the heaviest tiles of a causal launch
+// (the last query tiles, or the first key tiles) are dispatched first.
+
+// Entries a list of `tile`-row tiles needs at most: sum_s ceil(L_s / tile)
+// <= (total + nseq (tile - 1)) / tile.
+inline long long varlen_list_entries(long long total, int nseq, int tile) {
+  return (total + (long long)nseq * (tile - 1)) / tile;
+}
+
+inline size_t varlen_list_bytes(long long total, int nseq, int tile) {
+  return align_up((size_t)varlen_list_entries(total, nseq, tile) * 2 * sizeof(int), 256);
+}
+
+// Enqueues the list build: cu (nseq + 1) prefix sums of the lengths on the
+// device, levels = ceil(max_len / tile) (tiles past it are not listed).
+int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int* list,
+                    long long n_entries, hipStream_t st);
+
+// Work-group of a list launch: entry blockIdx.x / n_heads, head
+// blockIdx.x % n_heads.  Returns false for an unused entry (uniform over the
+// work-group).
+__device__ __forceinline__ bool tile_from_list(const int* list, int n_heads, TileId& r) {
+  const int e = (int)blockIdx.x / n_heads;
+  r.h = (int)blockIdx.x % n_heads;
+  r.b = list[2 * e];
+  r.t = list[2 * e + 1];
+  return r.b >= 0;
+}
+
 // ---- kernel timing (implemented in fa_api.hip) ----
 void prof_before(int kind, hipStream_t s);
 void prof_after(int kind, hipStream_t s);

@@ -150,3 +150,67 @@ def test_sequence_isolation_bitwise():
     for x, y in zip(g1, g2):
         assert torch.equal(x[keep], y[keep])
     assert not torch.equal(o1[a:b], o2[a:b])
+
+
+def _tile_list(lengths, tile, levels, ascending):
+    """The tile list the library builds, written out in Python: level by level
+    (tile index t from levels - 1 down, or from 0 up), sequences in index
+    order within a level, every (sequence, t) with t < ceil(L / tile); then
+    (-1, -1) up to the bound (total + nseq (tile - 1)) // tile."""
+    n = [-(-L // tile) for L in lengths]
+    order = range(levels) if ascending else range(levels - 1, -1, -1)
+    out = [(s, t) for t in order for s, ns in enumerate(n) if ns > t]
+    bound = (sum(lengths) + len(lengths) * (tile - 1)) // tile
+    return np.array(out + [(-1, -1)] * (bound - len(out)), dtype=np.int32).reshape(-1, 2)
+
+
+@pytest.mark.parametrize("shape", ["many_short", "very_long", "mixed"])
+def test_tile_lists_bit_exact(shape):
+    """The (sequence, tile) lists of the forward (128-row query tiles) and the
+    backward (query tiles for dQ, 256-key tiles for dK/dV, key tiles heaviest
+    first = from tile 0 for causal) equal the Python construction, entry for
+    entry, including lengths of 0, more levels than one pass of the list
+    kernel (1024) and more sequences than its threads."""
+    rng = np.random.default_rng({"many_short": 1, "very_long": 2, "mixed": 3}[shape])
+    if shape == "many_short":
+        lq = [int(x) for x in rng.integers(0, 300, size=2500)]
+    elif shape == "very_long":
+        lq = [140000, 0, 5, 300]
+    else:
+        lq = [int(x) for x in rng.integers(0, 5000, size=40)] + [0, 129, 128, 127, 1]
+    lk = [L + int(rng.integers(0, 3)) if L else 0 for L in lq]
+    c = varlen_case(lq, lk, Hq=1, Hkv=1, D=32, seed=45, causal=True, window=(32, 0))
+    q, k, v, do = (t.to(DEV) for t in (c.q, c.k, c.v, c.dout))
+    cq, ck = c.cu_seqlens_q.to(DEV), c.cu_seqlens_k.to(DEV)
+    L = fa.lib()
+    nseq, tq, tk = len(lq), q.shape[0], k.shape[0]
+    wsf = torch.full((L.fa_fwd_varlen_workspace_size(nseq, tq, 1, 32),), 0x7F, dtype=torch.uint8, device=DEV)
+    wsb = torch.full((L.fa_bwd_varlen_workspace_size(nseq, tq, tk, 1, 32, 0),), 0x7F, dtype=torch.uint8,
+                     device=DEV)
+    say("varlen tile lists", shape, nseq, tq, tk)
+    kw = dict(scale=c.scale, causal=True, window=(32, 0))
+    out, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, c.max_seqlen_q, c.max_seqlen_k, workspace=wsf, **kw)
+    fa.fa_bwd_varlen(q, k, v, out, do, lse, cq, ck, c.max_seqlen_q, c.max_seqlen_k, workspace=wsb, **kw)
+    torch.cuda.synchronize()
+    want_q = _tile_list(lq, 128, -(-c.max_seqlen_q // 128), False)
+    want_k = _tile_list(lk, 256, -(-c.max_seqlen_k // 256), True)
+    got_f = wsf.cpu().numpy().view(np.int32)[:want_q.size].reshape(-1, 2)
+    np.testing.assert_array_equal(got_f, want_q)
+    rows = -(-(tq * 4) // 256) * 256
+    lists = wsb.cpu().numpy()[2 * rows:]
+    q_bytes = -(-(want_q.size * 4) // 256) * 256
+    np.testing.assert_array_equal(lists[:want_q.size * 4].view(np.int32).reshape(-1, 2), want_q)
+    np.testing.assert_array_equal(lists[q_bytes:q_bytes + want_k.size * 4].view(np.int32).reshape(-1, 2), want_k)
+    # the launch itself is still right (a window of 32 keys keeps the check cheap)
+    pick = [i for i, n in enumerate(lq) if n][:3] + [len(lq) - 1]
+    cqs = c.cu_seqlens_q.tolist()
+    cks = c.cu_seqlens_k.tolist()
+    for s in pick:
+        a, b, ka, kb = cqs[s], cqs[s + 1], cks[s], cks[s + 1]
+        if b == a:
+            continue
+        rows_s = sorted(set([0, (b - a) // 2, b - a - 1]))
+        ro, rl = attention_fwd(c.q[a:b][None], c.k[ka:kb][None], c.v[ka:kb][None], c.scale, True, (32, 0),
+                               q_rows=rows_s)
+        assert_out(out[a:b][None][:, rows_s], ro[:, rows_s], torch.bfloat16)
+        assert_lse(lse[:, a:b][None][:, :, rows_s], rl[:, :, rows_s])

@@ -45,7 +45,14 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     # two float32 row arrays (row term, LSE in log2 units), each padded to 256 bytes
     assert lib.fa_bwd_workspace_size(2, 512, 512, 16, 16, 128, 0) == 2 * (2 * 16 * 512 * 4)
-    assert lib.fa_bwd_varlen_workspace_size(1000, 3, 128, 0) == 2 * 12032  # 12000 rounded up to 256
+    # varlen backward: two row arrays, then the 128-row query-tile list and the
+    # 256-key tile list (8 bytes per entry, at most (total + nseq (tile - 1)) / tile entries)
+    rows = 2 * 12032  # 1000 * 3 * 4 = 12000 rounded up to 256
+    q_list = -(-((1000 + 5 * 127) // 128) * 8 // 256) * 256
+    k_list = -(-((900 + 5 * 255) // 256) * 8 // 256) * 256
+    assert lib.fa_bwd_varlen_workspace_size(5, 1000, 900, 3, 128, 0) == rows + q_list + k_list
+    assert lib.fa_fwd_varlen_workspace_size(5, 1000, 3, 128) == q_list
+    assert lib.fa_fwd_varlen_workspace_size(5, 0, 3, 128) == 0
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 1) == 0
     assert lib.fa_kvcache_workspace_size(8, 1, 32, 128, 16) == 8 * 32 * 16 * 128 * 4 + 8 * 32 * 16 * 4
     # num_splits = 0 (automatic) is sized for the largest automatic choice, 32
@@ -116,10 +123,15 @@ def test_kvcache_rejects(lib):
 
 
 def test_varlen_rejects(lib):
-    st = lib.fa_fwd_varlen(F, F, F, F, F, F, F, 0, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, None)
+    st = lib.fa_fwd_varlen(F, F, F, F, F, F, F, 0, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, F,
+                           1 << 20, None)
     assert st == 1  # nseq = 0
-    st = lib.fa_fwd_varlen(F, F, F, F, F, None, F, 1, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, None)
+    st = lib.fa_fwd_varlen(F, F, F, F, F, None, F, 1, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, F,
+                           1 << 20, None)
     assert st == 1  # cu_seqlens_q missing
+    st = lib.fa_fwd_varlen(F, F, F, F, F, F, F, 1, 8, 8, 8, 8, 2, 2, 128, 1, 0.1, 0, -1, -1, 0.0, None, None,
+                           0, None)
+    assert st == 3  # the tile list needs a workspace
 
 
 def test_noalloc_rejects_requests_beyond_its_scratch(lib):
