@@ -459,13 +459,12 @@ def run_decode(args, torch, fa, splits=16):
         [1, 4, splits, 0] if splits not in (1, 4, 0) else [1, 4, 0])
     reps = max(12, args.steps * 6)
 
-    def timed(ns, ws, pool_of, before=None):
-        """Median call time (HIP events) and mean split/combine kernel times
-        over `reps` calls; call i reads pool pool_of(i)."""
-        fa.profiler_enable(4 * reps)
-        fa.profiler_reset()
-        evs = []
-        for i in range(reps):
+    def timed(ns, ws, pool_of, before=None, warm=0):
+        """`warm` untimed calls; then `reps` calls each between two HIP events
+        (median call time, no per-kernel events); then `reps` more calls with
+        the library's per-kernel events on (split/combine kernel means).  Call
+        i reads pool pool_of(i)."""
+        def run(i):
             if before is not None:
                 before(i)
             kc, vc = pools[pool_of(i)]
@@ -474,9 +473,17 @@ def run_decode(args, torch, fa, splits=16):
             fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
                               scale=c.scale, workspace=ws)
             e1.record()
-            evs.append((e0, e1))
+            return e0, e1
+        for i in range(warm):
+            run(i)
+        evs = [run(warm + i) for i in range(reps)]
         torch.cuda.synchronize()
         call_ms = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+        fa.profiler_enable(4 * reps)
+        fa.profiler_reset()
+        for i in range(reps):
+            run(warm + reps + i)
+        torch.cuda.synchronize()
         prof = fa.profiler_read()
         fa.profiler_disable()
         split_ms = prof["decode_split"][0] / max(1, prof["decode_split"][1])
@@ -487,19 +494,14 @@ def run_decode(args, torch, fa, splits=16):
         ws = torch.empty(max(1, fa.lib().fa_kvcache_workspace_size(8, 1, 32, 128, ns)), device=dev,
                          dtype=torch.uint8)
         rot = lambda i: i % DECODE_POOLS
-        for i in range(2 * DECODE_POOLS):  # warm-up (rotated)
-            kc, vc = pools[rot(i)]
-            fa.fa_fwd_kvcache(q, kc, vc, sl, kn, vn, bt, cos, sin, 128, num_splits=ns, out=out, lse=lse,
-                              scale=c.scale, workspace=ws)
-        torch.cuda.synchronize()
-        call_ms, split_ms, comb_ms = timed(ns, ws, rot)
+        call_ms, split_ms, comb_ms = timed(ns, ws, rot, warm=2 * DECODE_POOLS)
         r = {"num_splits": ns, "us_per_call": round(call_ms * 1e3, 1),
              "GBps": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
              "split_kernel_us": round(split_ms * 1e3, 2), "combine_kernel_us": round(comb_ms * 1e3, 2),
              "split_kernel_GBps": round(nbytes / (split_ms * 1e-3) / 1e9, 1)}
         if not args.cold_only:
-            w_call, w_split, _ = timed(ns, ws, lambda i: 0)
-            f_call, f_split, _ = timed(ns, ws, lambda i: 0, before=lambda i: scratch.fill_(i & 255))
+            w_call, w_split, _ = timed(ns, ws, lambda i: 0, warm=2)
+            f_call, f_split, _ = timed(ns, ws, lambda i: 0, before=lambda i: scratch.fill_(i & 255), warm=2)
             r.update({"warm_us_per_call": round(w_call * 1e3, 1), "warm_GBps": round(nbytes / w_call / 1e6, 1),
                       "warm_split_kernel_GBps": round(nbytes / w_split / 1e6, 1),
                       "after_write_flush_us_per_call": round(f_call * 1e3, 1),
@@ -622,16 +624,18 @@ KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
 
 def _pmc_rows(d, counter):
     """(kernel name, dispatch id) -> value summed over the counter's instances,
-    from a rocprofv3 --pmc --output-format csv directory."""
+    from rocprofv3 --pmc --output-format csv directories (comma-separated)."""
     import csv
     import glob
     out = {}
-    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    paths = [p for one in d.split(",") for p in
+             glob.glob(os.path.join(one, "**", "*counter_collection.csv"), recursive=True)]
+    for path in paths:
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                key = (r["Kernel_Name"], path, r["Dispatch_Id"])
                 out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
     return out
 
@@ -645,14 +649,14 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
 
     def per_kernel(rows):
         acc = {}
-        for (name, _), v in rows.items():
+        for (name, _, _), v in rows.items():
             for pat, key in KERNEL_KEYS:
                 if pat in name:
                     acc.setdefault(key, []).append(v)
         return {k: statistics.mean(v) for k, v in acc.items()}
 
     def copy_kib(rows):
-        vals = [v for (name, _), v in rows.items() if "copy" in name.lower()]
+        vals = [v for (name, _, _), v in rows.items() if "copy" in name.lower()]
         return statistics.median(vals) if vals else None
 
     f_cal, w_cal = copy_kib(_pmc_rows(cal_fetch_dir, "FETCH_SIZE")), copy_kib(_pmc_rows(cal_write_dir, "WRITE_SIZE"))

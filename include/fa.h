@@ -344,7 +344,8 @@ size_t fa_kvcache_noalloc_max_bytes(void);
 /*
  * Kernel timing (for benchmarks and profiles).  When enabled, every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the
- * launch stream.  fa_profiler_read synchronises on the recorded events and
+ * launch stream (created without the system-scope fence, which would add the
+ * write-back of the kernel's output to the interval).  fa_profiler_read synchronises on the recorded events and
  * returns, per kernel kind, the summed duration in milliseconds and the
  * number of launches since the last reset.  Event pairs come from a pool
  * created by fa_profiler_enable(1, capacity); launches past the capacity are

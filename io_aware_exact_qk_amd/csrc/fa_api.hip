@@ -78,8 +78,11 @@ extern "C" int fa_profiler_enable(int enable, int capacity) {
   if (capacity < 1) return FA_ERR_INVALID_ARG;
   g_prof.ev.resize(2 * (size_t)capacity);
   g_prof.kind.assign(capacity, 0);
+  // timing-only events: without the system-scope release fence a record
+  // would otherwise add (writing back the kernel's dirty lines), the pair
+  // brackets the kernel's own execution
   for (size_t i = 0; i < g_prof.ev.size(); ++i) {
-    if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+    if (hipEventCreateWithFlags(&g_prof.ev[i], hipEventDisableSystemFence) != hipSuccess) {
       g_prof.ev.resize(i);
       prof_destroy();
       return FA_ERR_LAUNCH;
