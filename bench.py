@@ -97,11 +97,31 @@ def recorded_traffic(kernel):
 
 
 # ---------------------------------------------------------------------------
-def time_ms(torch, fn, reps=3, warm=1):
+WARM_MS = 100.0
+
+
+def warm_for(torch, fn, ms=WARM_MS):
+    """Calls `fn` back to back for at least `ms` of wall time.  After an idle
+    spell (input set-up on the host) the GPU clock swings for tens of
+    milliseconds of load before it settles: a kernel traced right after one
+    ran 589, 766, 674 ... 600 us on successive identical calls.  A leg timed
+    straight after set-up would time that swing, not the kernels."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_ms(torch, fn, reps=3, warm=1, warm_ms=WARM_MS):
     """Mean time of `fn` over `reps` calls, from HIP events on the current
-    stream, after `warm` untimed calls."""
+    stream, after `warm` untimed calls and at least `warm_ms` of back-to-back
+    calls."""
     for _ in range(warm):
         fn()
+    if warm_ms > 0:
+        warm_for(torch, fn, warm_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -143,7 +163,7 @@ def per_config(torch, fa, cases, reps=3):
     per = []
     for t in cases:
         for causal in (False, True):
-            ms = time_ms(torch, lambda: fwdbwd_once(fa, t, causal), reps=reps, warm=0)
+            ms = time_ms(torch, lambda: fwdbwd_once(fa, t, causal), reps=reps)
             fl = 14 * t["D"] * visible_pairs(t["B"], t["H"], t["S"], causal)
             per.append({"S": t["S"], "B": t["B"], "H": t["H"], "D": t["D"], "causal": causal,
                         "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)})
@@ -180,14 +200,7 @@ def run_fwdbwd(args, torch, fa):
                 fa.fa_bwd_dropout(t["q"], t["k"], t["v"], t["out"], t["do"], t["lse"], 0.1, 1234, 0,
                                   dq=t["dq"], dk=t["dk"], dv=t["dv"], scale=scale, causal=causal,
                                   workspace=t["ws"])
-            one_drop()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(3):
-                one_drop()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 3
+            ms = time_ms(torch, one_drop, reps=3)
             fl = 14 * D * visible_pairs(t["B"], H, t["S"], causal)
             drop.append({"S": t["S"], "B": t["B"], "causal": causal, "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
@@ -204,14 +217,7 @@ def run_fwdbwd(args, torch, fa):
             def one_d():
                 o_, l_ = fa.fa_fwd(q_, k_, v_, scale=1.0 / math.sqrt(Dh), causal=causal)
                 fa.fa_bwd(q_, k_, v_, o_, do_, l_, scale=1.0 / math.sqrt(Dh), causal=causal, workspace=ws_)
-            one_d()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(3):
-                one_d()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 3
+            ms = time_ms(torch, one_d, reps=3)
             fl = 14 * Dh * visible_pairs(4, Hh, 4096, causal)
             by_d.append({"D": Dh, "H": Hh, "S": 4096, "B": 4, "causal": causal, "ms": round(ms, 4),
                          "tflops": round(fl / ms / 1e9, 1)})
@@ -238,14 +244,7 @@ def run_fwdbwd(args, torch, fa):
                     else:
                         fa.fa_fwd_fp8(f8["q"], f8["k"], f8["v"], f8["dq"], f8["dk"], f8["dv"], out=t["out"],
                                       lse=t["lse"], scale=scale, causal=causal, workspace=ws8)
-                one_f()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(5):
-                    one_f()
-                e1.record()
-                torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / 5
+                ms = time_ms(torch, one_f, reps=5)
                 res[kind + "_ms"] = round(ms, 4)
                 res[kind + "_tflops"] = round(4 * D * visible_pairs(t["B"], H, t["S"], causal) / ms / 1e9, 1)
             fp8.append(res)

@@ -52,6 +52,7 @@ struct BwdParams {
   const float* alibi;
   int wl, wr;
   int n_tiles, n_heads, n_batch, reverse, balanced;
+  int group;  // balanced: pairs per XCD group (tile_id)
   const int* tiles;  // varlen tile list (entries x 2 ints), or NULL
   DropSpec drop; // DROP kernels only
 };
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   if (p.tiles) {
     if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
   } else {
-    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, false);
+    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, false, p.group);
   }
   const int tk = tid3.t, hk = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
   if (p.tiles) {
     if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
   } else {
-    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, p.reverse != 0);
+    tid3 = tile_id(p.n_tiles, p.n_heads, p.n_batch, p.balanced != 0, p.reverse != 0, p.group);
   }
   const int tq = tid3.t, h = tid3.h, b = tid3.b;
   const SeqBounds sb = seq_bounds(p, b);
@@ -656,6 +657,7 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   kv.n_batch = kv_list ? 1 : nbatch;
   kv.reverse = 0;
   kv.balanced = causal ? 1 : 0;
+  kv.group = kTileGroup;
   BwdParams dq = base;
   dq.tiles = q_list;
   dq.n_tiles = q_list ? (int)q_entries : (max_sq + 127) / 128;
@@ -663,6 +665,7 @@ static int run_bwd(BwdParams base, int D, int dtype, int Hkv, int max_sq, int ma
   dq.n_batch = q_list ? 1 : nbatch;
   dq.reverse = causal ? 1 : 0;
   dq.balanced = causal ? 1 : 0;
+  dq.group = kTileGroup;
   const long long nwg_kv = (long long)kv.n_tiles * kv.n_heads * kv.n_batch;
   const long long nwg_q = (long long)dq.n_tiles * dq.n_heads * dq.n_batch;
   if (nwg_kv > 0x7fffffffLL || nwg_q > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;

@@ -48,6 +48,7 @@ struct FwdParams {
   int wl, wr;           // window, causal folded into wr = 0
   int n_qtiles, n_heads, n_batch;
   int reverse;          // causal: heaviest tiles first
+  int group;            // causal: pairs per XCD group (tile_id)
   const int* tiles;     // varlen tile list (entries x 2 ints), or NULL
   DropSpec drop;        // DROP kernels only
   // FP8 kernels: q and k are OCP e4m3 bytes, v the bfloat16 copy of the fp8
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
   if (p.tiles) {
     if (!tile_from_list(p.tiles, p.n_heads, tid3)) return;  // unused list entry
   } else {
-    tid3 = tile_id(p.n_qtiles, p.n_heads, p.n_batch, p.reverse != 0, p.reverse != 0);
+    tid3 = tile_id(p.n_qtiles, p.n_heads, p.n_batch, p.reverse != 0, p.reverse != 0, p.group);
   }
   const int tq = tid3.t, h = tid3.h, b = tid3.b;
 
@@ -568,6 +569,7 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
     prm.n_batch = nbatch;
   }
   prm.reverse = causal ? 1 : 0;
+  prm.group = kTileGroup;
   // a varlen tile list replaces the (tile, head, sequence) grid: n_qtiles
   // then counts list entries and n_batch is 1
   const long long nwg = (long long)prm.n_qtiles * prm.n_heads * prm.n_batch;

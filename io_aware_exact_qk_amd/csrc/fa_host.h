@@ -61,20 +61,39 @@ struct TileId {
 //  * default: the hardware id is remapped so that each XCD receives one
 //    contiguous block of logical tiles, which keeps tiles that share K/V (or
 //    Q/dO) rows on the same L2;
-//  * balanced (causal launches, where tiles differ a lot in work): ids are
-//    taken tile-major in hardware order, so the heaviest tile of every
-//    (head, batch) is dispatched first and neighbouring tiles go to
-//    different XCDs.  heavy_last: the heaviest tile is the last one.
+//  * balanced (causal launches, where tiles differ a lot in work): tiles are
+//    taken level by level (tile index), so the heaviest tile of every
+//    (head, batch) pair is dispatched first.  Work-groups go to the 8 XCDs
+//    round-robin (hardware id mod 8), so XCD x serves the pairs
+//    p = x (mod 8), and with `group` > 0 it serves them `group` pairs at a
+//    time: all levels of one group of pairs, heaviest first, before the
+//    next group.  Tiles that share a pair's K/V (or Q/dO) rows then run
+//    together on one L2 instead of every pair of the XCD being in flight
+//    at once.  heavy_last: the heaviest tile is the last one.
 __device__ __forceinline__ TileId tile_id(int n_tiles, int n_heads, int n_batch, bool balanced,
-                                          bool heavy_last) {
+                                          bool heavy_last, int group) {
   TileId r;
   const int hw = (int)blockIdx.x;
   int t;
   if (balanced) {
-    const int hb = hw % (n_heads * n_batch);
-    t = hw / (n_heads * n_batch);
-    r.h = hb % n_heads;
-    r.b = hb / n_heads;
+    const int np = n_heads * n_batch;
+    int pair;
+    if (group > 0 && (np & 7) == 0) {
+      const int x = hw & 7, j = hw >> 3;  // XCD, dispatch order on it
+      const int per = np >> 3;            // pairs of this XCD
+      const int gsz = group * n_tiles;    // tiles of a full group
+      const int gi = j / gsz;
+      const int g0 = gi * group;
+      const int gn = min(group, per - g0);  // pairs of this group
+      const int rr = j - gi * gsz;
+      t = rr / gn;
+      pair = x + 8 * (g0 + rr % gn);
+    } else {
+      pair = hw % np;
+      t = hw / np;
+    }
+    r.h = pair % n_heads;
+    r.b = pair / n_heads;
   } else {
     const int n = n_tiles * n_heads * n_batch;
     const int per = n / 8;
@@ -86,6 +105,14 @@ __device__ __forceinline__ TileId tile_id(int n_tiles, int n_heads, int n_batch,
   r.t = heavy_last ? n_tiles - 1 - t : t;
   return r;
 }
+
+// Pairs per XCD group of a balanced launch.  Measured on the causal
+// fwd+bwd sweep (bf16, H = 16, D = 128, B*S = 16384) against no grouping:
+// 8 pairs per group takes 10% off the time at S = 512 (64 pairs per XCD),
+// 17% at 1K, 4% at 2K, and leaves S >= 4K (8 pairs or fewer per XCD)
+// unchanged; 1 or 2 pairs per group are slower at S >= 2K, where the last
+// group's heaviest tiles then start too late to finish with the rest.
+constexpr int kTileGroup = 8;
 
 // ---- varlen tile list (kernel in fa_fwd.hip) ----
 // A packed variable-length launch runs one work-group per (list entry, head)
