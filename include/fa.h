@@ -114,9 +114,13 @@ size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int 
  * sequence are left untouched.
  * Scheduling: a small kernel first writes, into the workspace, the list of
  * the real (sequence, tile) pairs from cu_seqlens (on the device, no host
- * synchronisation), level by level so that the heaviest tiles of a causal
- * launch come first; the attention kernels then run one work-group per
+ * synchronisation); the attention kernels then run one work-group per
  * (list entry, head) and no work-group for tiles past a sequence's end.
+ * With up to 4096 sequences the list takes the sequences longest first, in
+ * groups of max(1, 64 / heads), each group level by level with its heaviest
+ * causal tiles first (so about eight (sequence, head) pairs share each of
+ * the chip's eight L2 caches at a time); with more, it goes level by level
+ * over all sequences.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,

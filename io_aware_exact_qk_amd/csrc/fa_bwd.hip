@@ -841,14 +841,15 @@ static int bwd_varlen(const void* q, const void* k, const void* v, const void* o
     q_list = (int*)lists;
     q_entries = varlen_list_entries(total_q, nseq, 128);
     lists += varlen_list_bytes(total_q, nseq, 128);
-    st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, q_list, q_entries, s);
+    st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, Hq, q_list, q_entries, s);
     if (st) return st;
   }
   if (total_k > 0) {
     const int kk = dkdv_keys(D);
     kv_list = (int*)lists;
     kv_entries = varlen_list_entries(total_k, nseq, kk);
-    st = varlen_schedule(cu_seqlens_k, nseq, kk, (max_seqlen_k + kk - 1) / kk, causal != 0, kv_list, kv_entries, s);
+    st = varlen_schedule(cu_seqlens_k, nseq, kk, (max_seqlen_k + kk - 1) / kk, causal != 0, Hkv, kv_list,
+                         kv_entries, s);
     if (st) return st;
   }
   return run_bwd(p, D, dtype, Hkv, max_seqlen_q, max_seqlen_k, nseq, causal, s, q_list, q_entries, kv_list,

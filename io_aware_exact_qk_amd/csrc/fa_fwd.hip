@@ -611,7 +611,8 @@ static int run_fwd(FwdParams& prm, int D, int dtype, float scale, float softcap,
 }
 
 // ------------------------------------------------------ varlen tile list --
-// One work-group of 1024 threads writes the list (layout and order in
+// Level-major list (more than kListSortMax sequences).  One work-group of
+// 1024 threads writes the list (layout and order in
 // fa_host.h).  Levels are taken in passes of TP <= 1024; in a pass, thread
 // (lvl, c) owns level lvl and the c-th of 1024 / TP contiguous chunks of the
 // sequences: it counts the chunk's sequences with a tile at that level,
@@ -681,11 +682,112 @@ __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int* cu, in
   }
 }
 
-int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int* list,
+// Grouped list (nseq <= kListSortMax).  One work-group of 1024 threads:
+//  1. sorts the sequences by tile count, most first (ties: lower index
+//     first), with a bitonic sort of (count, index) keys in LDS;
+//  2. cuts the sorted order into groups of `group` sequences and gives each
+//     group its first slot (prefix sum of the groups' tile counts);
+//  3. writes each group level by level: entry (sorted rank r, tile t) goes
+//     to the group's first slot + the group's entries on levels before t +
+//     (r - first rank of the group), since every earlier rank of the group
+//     has at least as many tiles.
+__global__ __launch_bounds__(1024) void varlen_schedule_grouped_kernel(const int* cu, int nseq, int tile,
+                                                                      int levels, int ascending, int group,
+                                                                      int* list, int n_entries) {
+  __shared__ unsigned long long key[kListSortMax];
+  __shared__ int gsum[kListSortMax];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < nseq) P <<= 1;
+  for (int i = tid; i < P; i += 1024) {
+    unsigned long long kv = ~0ULL;
+    if (i < nseq) {
+      const int len = cu[i + 1] - cu[i];
+      const unsigned nt = len > 0 ? (unsigned)min((len + tile - 1) / tile, levels) : 0u;
+      kv = ((unsigned long long)(0x7fffffffu - nt) << 32) | (unsigned)i;
+    }
+    key[i] = kv;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long a = key[i], b = key[l];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  auto nt_of = [&](int r) { return (int)(0x7fffffffu - (unsigned)(key[r] >> 32)); };
+  const int ng = (nseq + group - 1) / group;
+  for (int g = tid; g < ng; g += 1024) {
+    int n = 0;
+    for (int r = g * group; r < min(nseq, (g + 1) * group); ++r) n += nt_of(r);
+    gsum[g] = n;
+  }
+  __syncthreads();
+  // exclusive prefix over the groups: each thread scans a contiguous run
+  const int per = (ng + 1023) / 1024;
+  const int g0 = min(ng, tid * per), g1 = min(ng, g0 + per);
+  int run = 0;
+  for (int g = g0; g < g1; ++g) run += gsum[g];
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int acc = part[tid] - run;
+  for (int g = g0; g < g1; ++g) {
+    const int n = gsum[g];
+    gsum[g] = acc;
+    acc += n;
+  }
+  const int total = part[1023];
+  __syncthreads();
+  for (int r = tid; r < nseq; r += 1024) {
+    const int nt = nt_of(r);
+    if (nt == 0) continue;
+    const int g = r / group, r0 = g * group, r1 = min(nseq, r0 + group);
+    const int sq = (int)(key[r] & 0xffffffffu);
+    for (int t = 0; t < nt; ++t) {
+      int pos = gsum[g] + (r - r0);
+      for (int m = r0; m < r1; ++m) {
+        const int nm = nt_of(m);
+        pos += ascending ? min(t, nm) : max(0, nm - 1 - t);
+      }
+      if (pos < n_entries) {  // cu_seqlens inconsistent with the totals: no write past the list
+        list[2 * pos] = sq;
+        list[2 * pos + 1] = t;
+      }
+    }
+  }
+  for (int e = total + tid; e < n_entries; e += 1024) {
+    list[2 * e] = -1;
+    list[2 * e + 1] = -1;
+  }
+}
+
+int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int heads, int* list,
                     long long n_entries, hipStream_t st) {
   if (n_entries > 0x3fffffffLL || levels < 0) return FA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, tile, levels,
-                     ascending ? 1 : 0, list, (int)n_entries);
+  if (nseq <= kListSortMax) {
+    hipLaunchKernelGGL(varlen_schedule_grouped_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, tile, levels,
+                       ascending ? 1 : 0, varlen_list_group(heads), list, (int)n_entries);
+  } else {
+    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, tile, levels,
+                       ascending ? 1 : 0, list, (int)n_entries);
+  }
   return launch_status();
 }
 
@@ -747,7 +849,7 @@ static int fwd_varlen(const void* q, const void* k, const void* v, void* out, fl
   if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
   // the real (sequence, 128-row tile) pairs, heaviest level first
   const long long entries = varlen_list_entries(total_q, nseq, 128);
-  st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, (int*)workspace, entries,
+  st = varlen_schedule(cu_seqlens_q, nseq, 128, (max_seqlen_q + 127) / 128, false, Hq, (int*)workspace, entries,
                        (hipStream_t)stream);
   if (st) return st;
   FwdParams prm{};

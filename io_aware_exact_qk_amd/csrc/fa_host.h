@@ -114,15 +114,23 @@ __device__ __forceinline__ TileId tile_id(int n_tiles, int n_heads, int n_batch,
 // group's heaviest tiles then start too late to finish with the rest.
 constexpr int kTileGroup = 8;
 
-// ---- varlen tile list (kernel in fa_fwd.hip) ----
+// ---- varlen tile list (kernels in fa_fwd.hip) ----
 // A packed variable-length launch runs one work-group per (list entry, head)
 // instead of one per (max_seqlen tile, head, sequence): the list holds the
 // real (sequence, tile) pairs only, built on the device from cu_seqlens.
 // Entry e is the int pair list[2e] = sequence, list[2e + 1] = tile index
-// within it; unused trailing entries hold -1.  Order: level by level (tile
-// index t from the highest down, or from 0 up with ascending), sequences in
-// index order within a level, so the heaviest tiles of a causal launch
-// (the last query tiles, or the first key tiles) are dispatched first.
+// within it; unused trailing entries hold -1.  Order, for nseq <=
+// kListSortMax: the sequences sorted by tile count, most first (ties: lower
+// index first), cut into groups of varlen_list_group(heads) sequences; each
+// group level by level (tile index t from the highest down, or from 0 up
+// with ascending), sequences in sorted order within a level.  Heavy tiles
+// of a causal launch (the last query tiles, or the first key tiles) of the
+// longest sequences come first, and each XCD (work-group id mod 8, so heads
+// h = x mod 8 when heads is a multiple of 8) holds about eight (sequence,
+// head) pairs in flight, as kTileGroup does for dense launches.  More
+// sequences: level by level over all sequences, index order within a level.
+constexpr int kListSortMax = 4096;
+inline int varlen_list_group(int heads) { return heads >= 64 ? 1 : 64 / (heads > 0 ? heads : 1); }
 
 // Entries a list of `tile`-row tiles needs at most: sum_s ceil(L_s / tile)
 // <= (total + nseq (tile - 1)) / tile.
@@ -136,7 +144,7 @@ inline size_t varlen_list_bytes(long long total, int nseq, int tile) {
 
 // Enqueues the list build: cu (nseq + 1) prefix sums of the lengths on the
 // device, levels = ceil(max_len / tile) (tiles past it are not listed).
-int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int* list,
+int varlen_schedule(const int* cu, int nseq, int tile, int levels, bool ascending, int heads, int* list,
                     long long n_entries, hipStream_t st);
 
 // Work-group of a list launch: entry blockIdx.x / n_heads, head

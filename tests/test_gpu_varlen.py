@@ -152,51 +152,72 @@ def test_sequence_isolation_bitwise():
     assert not torch.equal(o1[a:b], o2[a:b])
 
 
-def _tile_list(lengths, tile, levels, ascending):
-    """The tile list the library builds, written out in Python: level by level
-    (tile index t from levels - 1 down, or from 0 up), sequences in index
-    order within a level, every (sequence, t) with t < ceil(L / tile); then
-    (-1, -1) up to the bound (total + nseq (tile - 1)) // tile."""
-    n = [-(-L // tile) for L in lengths]
-    order = range(levels) if ascending else range(levels - 1, -1, -1)
-    out = [(s, t) for t in order for s, ns in enumerate(n) if ns > t]
+def _tile_list(lengths, tile, levels, ascending, heads):
+    """The tile list the library builds, written out in Python.  Every
+    (sequence, t) with t < min(ceil(L / tile), levels).  Up to 4096
+    sequences: sequences sorted by that tile count, most first (ties: lower
+    index first), in groups of 64 // heads (at least 1); each group level by
+    level (t from its highest down, or from 0 up), sorted order within a
+    level.  More sequences: level by level (levels - 1 down, or 0 up),
+    index order within a level.  Then (-1, -1) up to the bound
+    (total + nseq (tile - 1)) // tile."""
+    n = [min(-(-L // tile), levels) for L in lengths]
+    if len(n) <= 4096:
+        grp = max(1, 64 // heads)
+        order = sorted(range(len(n)), key=lambda s: (-n[s], s))
+        out = []
+        for g0 in range(0, len(n), grp):
+            members = order[g0:g0 + grp]
+            top = max(n[s] for s in members)
+            for t in (range(top) if ascending else range(top - 1, -1, -1)):
+                out += [(s, t) for s in members if n[s] > t]
+    else:
+        lv = range(levels) if ascending else range(levels - 1, -1, -1)
+        out = [(s, t) for t in lv for s, ns in enumerate(n) if ns > t]
     bound = (sum(lengths) + len(lengths) * (tile - 1)) // tile
     return np.array(out + [(-1, -1)] * (bound - len(out)), dtype=np.int32).reshape(-1, 2)
 
 
-@pytest.mark.parametrize("shape", ["many_short", "very_long", "mixed"])
+@pytest.mark.parametrize("shape", ["many_short", "very_long", "mixed", "gqa", "very_many"])
 def test_tile_lists_bit_exact(shape):
     """The (sequence, tile) lists of the forward (128-row query tiles) and the
     backward (query tiles for dQ, 256-key tiles for dK/dV, key tiles heaviest
     first = from tile 0 for causal) equal the Python construction, entry for
-    entry, including lengths of 0, more levels than one pass of the list
-    kernel (1024) and more sequences than its threads."""
-    rng = np.random.default_rng({"many_short": 1, "very_long": 2, "mixed": 3}[shape])
+    entry, including lengths of 0, sequences longer than 1024 tiles, group
+    sizes 64 (one head), 4 and 32 (16 query heads, 2 K/V heads), and more
+    sequences than the sorted construction takes (the level-by-level one)."""
+    rng = np.random.default_rng({"many_short": 1, "very_long": 2, "mixed": 3, "gqa": 4, "very_many": 5}[shape])
+    Hq = Hkv = 1
     if shape == "many_short":
         lq = [int(x) for x in rng.integers(0, 300, size=2500)]
     elif shape == "very_long":
         lq = [140000, 0, 5, 300]
+    elif shape == "gqa":
+        lq = [int(x) for x in rng.integers(0, 1500, size=60)] + [0, 256, 255]
+        Hq, Hkv = 16, 2
+    elif shape == "very_many":
+        lq = [int(x) for x in rng.integers(0, 40, size=5000)] + [700]
     else:
         lq = [int(x) for x in rng.integers(0, 5000, size=40)] + [0, 129, 128, 127, 1]
     lk = [L + int(rng.integers(0, 3)) if L else 0 for L in lq]
-    c = varlen_case(lq, lk, Hq=1, Hkv=1, D=32, seed=45, causal=True, window=(32, 0))
+    c = varlen_case(lq, lk, Hq=Hq, Hkv=Hkv, D=32, seed=45, causal=True, window=(32, 0))
     q, k, v, do = (t.to(DEV) for t in (c.q, c.k, c.v, c.dout))
     cq, ck = c.cu_seqlens_q.to(DEV), c.cu_seqlens_k.to(DEV)
     L = fa.lib()
     nseq, tq, tk = len(lq), q.shape[0], k.shape[0]
-    wsf = torch.full((L.fa_fwd_varlen_workspace_size(nseq, tq, 1, 32),), 0x7F, dtype=torch.uint8, device=DEV)
-    wsb = torch.full((L.fa_bwd_varlen_workspace_size(nseq, tq, tk, 1, 32, 0),), 0x7F, dtype=torch.uint8,
+    wsf = torch.full((L.fa_fwd_varlen_workspace_size(nseq, tq, Hq, 32),), 0x7F, dtype=torch.uint8, device=DEV)
+    wsb = torch.full((L.fa_bwd_varlen_workspace_size(nseq, tq, tk, Hq, 32, 0),), 0x7F, dtype=torch.uint8,
                      device=DEV)
     say("varlen tile lists", shape, nseq, tq, tk)
     kw = dict(scale=c.scale, causal=True, window=(32, 0))
     out, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, c.max_seqlen_q, c.max_seqlen_k, workspace=wsf, **kw)
     fa.fa_bwd_varlen(q, k, v, out, do, lse, cq, ck, c.max_seqlen_q, c.max_seqlen_k, workspace=wsb, **kw)
     torch.cuda.synchronize()
-    want_q = _tile_list(lq, 128, -(-c.max_seqlen_q // 128), False)
-    want_k = _tile_list(lk, 256, -(-c.max_seqlen_k // 256), True)
+    want_q = _tile_list(lq, 128, -(-c.max_seqlen_q // 128), False, Hq)
+    want_k = _tile_list(lk, 256, -(-c.max_seqlen_k // 256), True, Hkv)
     got_f = wsf.cpu().numpy().view(np.int32)[:want_q.size].reshape(-1, 2)
     np.testing.assert_array_equal(got_f, want_q)
-    rows = -(-(tq * 4) // 256) * 256
+    rows = -(-(Hq * tq * 4) // 256) * 256
     lists = wsb.cpu().numpy()[2 * rows:]
     q_bytes = -(-(want_q.size * 4) // 256) * 256
     np.testing.assert_array_equal(lists[:want_q.size * 4].view(np.int32).reshape(-1, 2), want_q)
