@@ -647,12 +647,22 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     import statistics
 
     def per_kernel(rows):
+        # fwd / bwd kernels: the timed step of a `--steps 1` run, i.e. the
+        # last 12 launches of each in dispatch order (the launches before it
+        # are warm-up and per-configuration timing, weighted differently);
+        # decode kernels: every launch (all cold calls with --cold-only)
         acc = {}
-        for (name, _, _), v in rows.items():
+        for (name, path, disp), v in rows.items():
             for pat, key in KERNEL_KEYS:
                 if pat in name:
-                    acc.setdefault(key, []).append(v)
-        return {k: statistics.mean(v) for k, v in acc.items()}
+                    acc.setdefault((key, path), []).append((int(disp), v))
+        per = {}
+        for (key, _), vals in acc.items():
+            vals.sort()
+            if not key.startswith("decode"):
+                vals = vals[-2 * len(SEQLENS):]
+            per.setdefault(key, []).extend(v for _, v in vals)
+        return {k: statistics.mean(v) for k, v in per.items()}
 
     def copy_kib(rows):
         vals = [v for (name, _, _), v in rows.items() if "copy" in name.lower()]
