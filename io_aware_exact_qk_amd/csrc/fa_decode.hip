@@ -686,8 +686,8 @@ extern "C" int fa_fwd_kvcache(const void* q, const void* k_new, const void* v_ne
   if (rotary_cos && (rotary_dim < 16 || rotary_dim % 16 != 0 || rotary_dim > D)) return FA_ERR_INVALID_ARG;
   if (rotary_cos && (!aligned4(rotary_cos) || !aligned4(rotary_sin))) return FA_ERR_INVALID_ARG;
   if (alibi_slopes && !aligned4(alibi_slopes)) return FA_ERR_INVALID_ARG;
-  // D = 256: the four-stage K register ring does not fit beside the query
-  // (high and low parts) and O registers
+  // D = 256: two stages of a wave's private 32-key K and V tiles would take
+  // 64 KB per wave, 256 KB for the four waves of a work-group (LDS: 160 KB)
   if (D == 256) return FA_ERR_UNSUPPORTED;
   // the G * Sq_new new queries of a K/V head are the 32 MFMA columns
   if ((long long)(Hq / Hkv) * Sq_new > 32) return FA_ERR_UNSUPPORTED;
