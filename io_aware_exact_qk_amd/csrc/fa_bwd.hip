@@ -129,14 +129,14 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
   constexpr int ROWT = 2 * 64 * 4;
   constexpr int STAGE = ROWT + 2 * TILE;
   // Two stage buffers and the V rows of the work-group's keys (B operand of
-  // dP = dO V^T) in two halves: distinct arrays, so that reads of one are
-  // never ordered behind the DMA into another.  Each V half is smaller than a
-  // stage, so the stages are placed first and every stage tile base stays
-  // below 64 KB, within the immediate offset of the LDS reads.
+  // dP = dO V^T): distinct arrays, so that reads of one are never ordered
+  // behind the DMA into another.  Every wave addresses its V rows from the
+  // one V array: a pointer chosen between two arrays at run time would let
+  // the compiler assume it may alias a stage and wait for the next stage's
+  // copy (vmcnt(0)) before the first V read of every tile.
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char vsm0[BC / 2 * D * 2];
-  __shared__ __attribute__((aligned(1024))) char vsm1[BC / 2 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vsm[BC * D * 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -168,14 +168,13 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
     const bool in = DG == D || (2 * c + g) * 8 < DG;
     kreg[c] = (key_ok && in) ? gload128(p.k + krow + (2 * c + g) * 8) : u32x4{0, 0, 0, 0};
   }
-  zero_pad<D, BC / 2, DG>(vsm0, tid, 64 * NW);
-  zero_pad<D, BC / 2, DG>(vsm1, tid, 64 * NW);
+  zero_pad<D, BC, DG>(vsm, tid, 64 * NW);
   zero_pad<D, BR, DG>(sm0 + ROWT, tid, 64 * NW);
   zero_pad<D, BR, DG>(sm0 + ROWT + TILE, tid, 64 * NW);
   zero_pad<D, BR, DG>(sm1 + ROWT, tid, 64 * NW);
   zero_pad<D, BR, DG>(sm1 + ROWT + TILE, tid, 64 * NW);
   // this wave's 32 V rows
-  const char* vw = (w < NW / 2 ? vsm0 : vsm1) + (32 * (w % (NW / 2))) * (D * 2);
+  const char* vw = vsm + (32 * w) * (D * 2);
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
@@ -339,8 +338,7 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
 
     // V rows past Sk hold a copy of the last row; their keys are masked
     const uint16_t* vsrc = p.v + (int64_t)sb.k_start * p.k_rstride + hk * DG;
-    dma_tile<D, BC / 2, NW, true, DG>(vsm0, vsrc, p.k_rstride, k0, Sk, w, lane);
-    dma_tile<D, BC / 2, NW, true, DG>(vsm1, vsrc, p.k_rstride, k0 + BC / 2, Sk, w, lane);
+    dma_tile<D, BC, NW, true, DG>(vsm, vsrc, p.k_rstride, k0, Sk, w, lane);
     issue(0, sm0);
     dma_wait();
     __syncthreads();
