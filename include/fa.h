@@ -117,10 +117,10 @@ size_t fa_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D, int 
  * synchronisation); the attention kernels then run one work-group per
  * (list entry, head) and no work-group for tiles past a sequence's end.
  * With up to 4096 sequences the list takes the sequences longest first, in
- * groups of max(1, 64 / heads), each group level by level with its heaviest
- * causal tiles first (so about eight (sequence, head) pairs share each of
- * the chip's eight L2 caches at a time); with more, it goes level by level
- * over all sequences.
+ * groups of max(1, 32 / heads), each group level by level with its heaviest
+ * causal tiles first (so about four (sequence, head) pairs share each of the
+ * chip's eight L2 caches at a time); with more, it goes level by level over
+ * all sequences.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,

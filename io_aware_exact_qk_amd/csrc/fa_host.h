@@ -126,11 +126,14 @@ constexpr int kTileGroup = 8;
 // with ascending), sequences in sorted order within a level.  Heavy tiles
 // of a causal launch (the last query tiles, or the first key tiles) of the
 // longest sequences come first, and each XCD (work-group id mod 8, so heads
-// h = x mod 8 when heads is a multiple of 8) holds about eight (sequence,
-// head) pairs in flight, as kTileGroup does for dense launches.  More
-// sequences: level by level over all sequences, index order within a level.
+// h = x mod 8 when heads is a multiple of 8) holds about four (sequence,
+// head) pairs in flight.  Measured at 16 heads (causal fwd+bwd) against
+// groups of 1, 3, 4, 8, 16 and all sequences: 2 sequences per group is best
+// or within noise of the best on 13 sequences of 448-4002 tokens, 16 of 2048
+// and 64 of 128-1024.  More sequences: level by level over all sequences,
+// index order within a level.
 constexpr int kListSortMax = 4096;
-inline int varlen_list_group(int heads) { return heads >= 64 ? 1 : 64 / (heads > 0 ? heads : 1); }
+inline int varlen_list_group(int heads) { return heads >= 32 ? 1 : 32 / (heads > 0 ? heads : 1); }
 
 // Entries a list of `tile`-row tiles needs at most: sum_s ceil(L_s / tile)
 // <= (total + nseq (tile - 1)) / tile.

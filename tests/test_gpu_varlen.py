@@ -156,14 +156,14 @@ def _tile_list(lengths, tile, levels, ascending, heads):
     """The tile list the library builds, written out in Python.  Every
     (sequence, t) with t < min(ceil(L / tile), levels).  Up to 4096
     sequences: sequences sorted by that tile count, most first (ties: lower
-    index first), in groups of 64 // heads (at least 1); each group level by
+    index first), in groups of 32 // heads (at least 1); each group level by
     level (t from its highest down, or from 0 up), sorted order within a
     level.  More sequences: level by level (levels - 1 down, or 0 up),
     index order within a level.  Then (-1, -1) up to the bound
     (total + nseq (tile - 1)) // tile."""
     n = [min(-(-L // tile), levels) for L in lengths]
     if len(n) <= 4096:
-        grp = max(1, 64 // heads)
+        grp = max(1, 32 // heads)
         order = sorted(range(len(n)), key=lambda s: (-n[s], s))
         out = []
         for g0 in range(0, len(n), grp):
@@ -184,7 +184,7 @@ def test_tile_lists_bit_exact(shape):
     backward (query tiles for dQ, 256-key tiles for dK/dV, key tiles heaviest
     first = from tile 0 for causal) equal the Python construction, entry for
     entry, including lengths of 0, sequences longer than 1024 tiles, group
-    sizes 64 (one head), 4 and 32 (16 query heads, 2 K/V heads), and more
+    sizes 32 (one head), 2 and 16 (16 query heads, 2 K/V heads), and more
     sequences than the sorted construction takes (the level-by-level one)."""
     rng = np.random.default_rng({"many_short": 1, "very_long": 2, "mixed": 3, "gqa": 4, "very_many": 5}[shape])
     Hq = Hkv = 1
