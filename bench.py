@@ -603,7 +603,7 @@ def run_cpu_baseline():
     from oracle import attention_fwd, attention_bwd
     from workloads import cfg2
     n = cpu_threads()
-    flops, secs = 0.0, 0.0
+    flops, secs, fwd_secs = 0.0, 0.0, 0.0
     with threadpool_limits(limits=n):
         for S in (512, 1024, 2048, 4096):
             c = cfg2(S, H, D, False)
@@ -611,13 +611,17 @@ def run_cpu_baseline():
             for causal in (False, True):
                 t0 = time.perf_counter()
                 attention_fwd(q, k, v, c.scale, causal)
+                t1 = time.perf_counter()
                 attention_bwd(q, k, v, do, c.scale, causal, check_delta=False)
                 secs += time.perf_counter() - t0
+                fwd_secs += t1 - t0
                 flops += CPU_HEADS * 14 * D * (pairs_causal(S) if causal else S * S)
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
             "sample": f"float64 numpy oracle, fwd+bwd of the batch-0 slice of heads 0..{CPU_HEADS - 1} of the "
                       "sweep inputs for S in {512,1K,2K,4K}, non-causal and causal; same 14*D*pairs flop count",
-            "seconds": round(secs, 2), "host": host_info()}
+            "seconds": round(secs, 2),
+            "fwd_value": round(flops * 4 / 14 / fwd_secs / 1e12, 6), "fwd_seconds": round(fwd_secs, 2),
+            "host": host_info()}
 
 
 def run_cpu_decode():
@@ -637,7 +641,7 @@ def run_cpu_decode():
     nbytes = decode_bytes(c.cache_seqlens.tolist(), 8, 32, 8, 128, 256)
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
             "sample": "the whole decode call (B=8, Hq=32, Hkv=8, D=128, page 256, cache lengths seed 5), "
-                      "float64 numpy oracle", "seconds": round(secs, 2), "bytes": nbytes}
+                      "float64 numpy oracle", "seconds": round(secs, 2), "bytes": nbytes, "host": host_info()}
 
 
 def run_copy_calibration(torch):
