@@ -545,7 +545,27 @@ def run_decode(args, torch, fa, splits=16):
         res[ns] = r
         log(f"decode splits={ns}: {r}")
     best = max(res.values(), key=lambda r: r["GBps"])
+    # a measured-achievable column: a plain device copy of 1 GiB (1 GiB read +
+    # 1 GiB written), median of 7 after 3 untimed; four buffers in rotation,
+    # so a copy reads what was written two copies (2 GiB of writes) earlier
+    copy = None
+    if not args.cold_only:
+        bufs = [torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(i) for i in range(4)]
+        ts = []
+        for i in range(10):
+            src, dst = bufs[i % 4], bufs[(i + 2) % 4]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        cms = sorted(a.elapsed_time(b) for a, b in ts[3:])[3]
+        copy = round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)
+        del bufs
     return {"workload": "decode bf16 B=8 Hq=32 Hkv=8 D=128 page=256 rotary128, cache_seqlens seed 5",
+            "copy_GBps": copy,
+            "split_kernel_frac_of_copy": round(best["split_kernel_GBps"] / copy, 4) if copy else None,
             "timing": f"cold: {DECODE_POOLS} independent cache pools read in rotation (HIP events, median "
                       f"call; kernel means); warm_*: back-to-back calls on one pool; after_write_flush_*: each "
                       "call after an untimed 1 GiB scratch write",
