@@ -518,11 +518,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(BwdParams
         }
         // element i of half kb: logit, mask (keys past Sk hold a copy of the
         // last key), P, and dS in place of dP
+        const LaneRange kr = keys_for_row(row_ok, ip, Sk, mask);
         auto elem = [&](int kb, int i) {
           const int j = j0 + 32 * kb + frag_row(i, g);
           float x = s[kb][i];
           if constexpr (SOFTCAP || ALIBI) x = logit2<SOFTCAP, ALIBI>(x, ip, j, p, slope_log2);
-          if constexpr (MASKED) x = (row_ok & visible(ip, j, Sk, mask)) ? x : -INFINITY;
+          if constexpr (MASKED) x = in_range(range_test(kr, j0 + 32 * kb + 4 * g), i) ? x : -INFINITY;
           const float pv = fast_exp2(fmaf(x, fs, -lse2));
           float dpv = dp[kb][i];
           if constexpr (DROP) dpv = drop_keep(kx[kb], i, p.drop.t) ? dpv * p.drop.scale : 0.0f;

@@ -396,6 +396,39 @@ __device__ __forceinline__ bool visible(int ip, int j, int Sk, MaskSpec m) {
   return (j < Sk) & ((m.wl < 0) | (j >= ip - m.wl)) & ((m.wr < 0) | (j <= ip + m.wr));
 }
 
+// The same mask in range form, for the elements of one lane: the keys
+// visible to a lane's query row form one interval [lo, hi], empty when
+// hi < lo.  Element i of a 32 x 32 block whose key is
+// base + frag_row(i, g) = (base + 4 g) + frag_c(i) is then visible iff
+// (uint32)(base + 4 g - lo + frag_c(i)) <= (uint32)(hi - lo):
+// an add with a constant, a compare and a select per element, instead of
+// the three compares and the lane-mask logic of visible().
+struct LaneRange {
+  int lo, hi;
+};
+
+// Keys visible to query position ip (none when !row_ok).
+__device__ __forceinline__ LaneRange keys_for_row(bool row_ok, int ip, int Sk, MaskSpec m) {
+  const int lo = m.wl >= 0 ? max(ip - m.wl, 0) : 0;
+  const int hi = m.wr >= 0 ? min(ip + m.wr, Sk - 1) : Sk - 1;
+  return {lo, row_ok ? hi : lo - 1};
+}
+
+struct RangeTest {
+  uint32_t a, w;
+};
+
+// base: the coordinate of element frag_c = 0 of this lane (block base + 4 g).
+__device__ __forceinline__ RangeTest range_test(LaneRange r, int base) {
+  if (r.hi < r.lo) return {0x80000000u, 0u};
+  return {(uint32_t)(base - r.lo), (uint32_t)(r.hi - r.lo)};
+}
+
+// frag_row(i, g) - 4 g: the element's offset that does not depend on the lane
+__device__ __forceinline__ constexpr int frag_c(int i) { return 8 * (i >> 2) + (i & 3); }
+
+__device__ __forceinline__ bool in_range(RangeTest t, int i) { return t.a + (uint32_t)frag_c(i) <= t.w; }
+
 // Block-level classification for query positions [ip0, ip1] and keys [j0, j1].
 // Returns 0 = nothing visible, 1 = partially visible, 2 = everything visible.
 __device__ __forceinline__ int classify(int ip0, int ip1, int j0, int j1, int Sk, MaskSpec m) {

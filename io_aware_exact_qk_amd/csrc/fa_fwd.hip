@@ -232,13 +232,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_kernel(FwdParams p)
       }
       const int cls = (wrow0 < Sq) ? classify(wrow0 + off, wrow1 + off, j0, j0 + BC - 1, Sk, mask) : 0;
       if (cls != 2) {
+        const LaneRange kr = keys_for_row(row_ok, ip, Sk, mask);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          const RangeTest rt = range_test(kr, j0 + 32 * kb + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = j0 + 32 * kb + frag_row(i, g);
-            sa[kb][i] = (row_ok & visible(ip, j, Sk, mask)) ? sa[kb][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i) sa[kb][i] = in_range(rt, i) ? sa[kb][i] : -INFINITY;
         }
       }
     };
