@@ -282,12 +282,9 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::NW, 1) void bwd_dkdv_kernel(BwdP
           }
         }
         if (cls == 1) {
+          const RangeTest rt = range_test(rows_for_key(key_ok, my_key, Sq, off, mask), r0 + 4 * g);
 #pragma unroll
-          for (int ii = 0; ii < 16; ++ii) {
-            const int row = r0 + frag_row(ii, g);
-            const bool ok = (row < Sq) & key_ok & visible(row + off, my_key, Sk, mask);
-            s[ii] = ok ? s[ii] : -INFINITY;
-          }
+          for (int ii = 0; ii < 16; ++ii) s[ii] = in_range(rt, ii) ? s[ii] : -INFINITY;
         }
         // dropout: kept weights enter dV and dP (scaled once at the end / here)
         uint32_t kx[4];

@@ -396,11 +396,12 @@ __device__ __forceinline__ bool visible(int ip, int j, int Sk, MaskSpec m) {
   return (j < Sk) & ((m.wl < 0) | (j >= ip - m.wl)) & ((m.wr < 0) | (j <= ip + m.wr));
 }
 
-// The same mask in range form, for the elements of one lane: the keys
-// visible to a lane's query row form one interval [lo, hi], empty when
-// hi < lo.  Element i of a 32 x 32 block whose key is
-// base + frag_row(i, g) = (base + 4 g) + frag_c(i) is then visible iff
-// (uint32)(base + 4 g - lo + frag_c(i)) <= (uint32)(hi - lo):
+// The same mask in range form, for the elements of one lane: the visible
+// values of the coordinate that varies along a lane's accumulator elements
+// (keys for a query row, or query rows for a key) form one interval
+// [lo, hi], empty when hi < lo.  Element i of a 32 x 32 block whose
+// coordinate is base + frag_row(i, g) = (base + 4 g) + frag_c(i) is then
+// visible iff (uint32)(base + 4 g - lo + frag_c(i)) <= (uint32)(hi - lo):
 // an add with a constant, a compare and a select per element, instead of
 // the three compares and the lane-mask logic of visible().
 struct LaneRange {
@@ -412,6 +413,14 @@ __device__ __forceinline__ LaneRange keys_for_row(bool row_ok, int ip, int Sk, M
   const int lo = m.wl >= 0 ? max(ip - m.wl, 0) : 0;
   const int hi = m.wr >= 0 ? min(ip + m.wr, Sk - 1) : Sk - 1;
   return {lo, row_ok ? hi : lo - 1};
+}
+
+// Query rows (within the sequence, below Sq) that see key j, where query
+// row r sits at position r + off (none when !key_ok).
+__device__ __forceinline__ LaneRange rows_for_key(bool key_ok, int j, int Sq, int off, MaskSpec m) {
+  const int lo = m.wr >= 0 ? max(j - m.wr - off, 0) : 0;
+  const int hi = m.wl >= 0 ? min(j + m.wl - off, Sq - 1) : Sq - 1;
+  return {lo, key_ok ? hi : lo - 1};
 }
 
 struct RangeTest {
